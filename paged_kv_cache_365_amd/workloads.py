@@ -1,0 +1,315 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only *draws inputs*: query vectors, K/V pool contents, block tables
+and context lengths.  It holds none of the attention arithmetic, so both the
+fp64 CPU oracle and the HIP library read the very same bytes from it.
+
+Layouts (they are the library's ABI, stated in ``include/pa.h``):
+
+* ``q``            ``[B][H_q][d]``            element dtype of the pool
+* ``k_pool/v_pool`` ``[num_blocks][H_kv][16][d]`` one (block, kv-head) tile of 16
+                    token rows is contiguous
+* ``block_tables`` ``int32 [B][max_blocks_per_seq]``; entry ``j`` of row ``s``
+                    is the physical block holding tokens ``16j .. 16j+15`` of
+                    sequence ``s``; entries past the live range are ``-1``
+* ``context_lens`` ``int32 [B]``
+
+Element storage: ``f32`` arrays are ``np.float32``, ``f16`` arrays are
+``np.float16``, ``bf16`` arrays are ``np.uint16`` holding the raw bfloat16 bits.
+
+Value recipe: every value is N(0,1), drawn by inverse CDF over 65,536
+equiprobable levels (a uniform 16-bit draw indexes a table of standard-normal
+quantiles at (i + 0.5) / 65536, so tails stop at about +-4.2 sigma), then rounded
+to nearest-even into the element dtype.  A plain ``standard_normal`` draw is about
+a hundred times slower on the host and would dominate every run at the 1 GB pool
+sizes used here.
+
+The five workload shapes follow the cases the pages discuss: 16-token blocks
+(the default block size stated on both PagedAttention pages), 7B-style MHA,
+70B-style GQA with 8 KV heads, a shared system-prompt prefix referenced by
+every block table, and a 32K long-context batch split into 512-token
+partitions.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+from scipy.special import ndtri
+
+BLOCK_SIZE = 16
+DTYPES = ("f32", "f16", "bf16")
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+# numpy storage type per element dtype (bf16 is carried as raw bits)
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+NAN_BITS = {"f32": np.uint32(0x7FC00000), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+
+
+# --------------------------------------------------------------------------
+# element encoding (input preparation only)
+# --------------------------------------------------------------------------
+def f64_to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to the storage form of ``dtype`` (nearest-even)."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        f = x.astype(np.float32)
+        u = f.view(np.uint32).astype(np.uint64)
+        rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        nan = np.isnan(f)
+        if nan.any():
+            rounded = np.where(nan, np.uint16(0x7FC0), rounded)
+        return rounded
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+_QUANTILES = ndtri((np.arange(65536, dtype=np.float64) + 0.5) / 65536.0)
+_TABLE_CACHE: dict = {}
+
+
+def _normal_table(dtype: str, gain: float = 1.0) -> np.ndarray:
+    key = (dtype, gain)
+    if key not in _TABLE_CACHE:
+        _TABLE_CACHE[key] = f64_to_storage(_QUANTILES * gain, dtype)
+    return _TABLE_CACHE[key]
+
+
+def normal(rng: np.random.Generator, shape, dtype: str, gain: float = 1.0) -> np.ndarray:
+    """N(0, gain^2) values in the storage form of ``dtype``."""
+    idx = rng.integers(0, 65536, size=shape, dtype=np.uint16)
+    return _normal_table(dtype, gain)[idx]
+
+
+def nan_fill(shape, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.full(shape, NAN_BITS["f32"], dtype=np.uint32).view(np.float32)
+    if dtype == "f16":
+        return np.full(shape, NAN_BITS["f16"], dtype=np.uint16).view(np.float16)
+    return np.full(shape, NAN_BITS["bf16"], dtype=np.uint16)
+
+
+def const_fill(shape, dtype: str, value: float) -> np.ndarray:
+    return np.full(shape, f64_to_storage(np.array(value), dtype), dtype=STORAGE[dtype])
+
+
+# --------------------------------------------------------------------------
+# workload container
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class Workload:
+    name: str
+    dtype: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    q: np.ndarray             # [B][H_q][d] storage dtype
+    k_pool: np.ndarray        # [NB][H_kv][16][d]
+    v_pool: np.ndarray        # [NB][H_kv][16][d]
+    block_tables: np.ndarray  # int32 [B][max_blocks_per_seq]
+    context_lens: np.ndarray  # int32 [B]
+    scale: float              # float32 value carried as a Python float
+    partition_size: int = 0   # 0 = single phase
+    prefix_blocks: int = 0    # number of leading table entries shared by all rows
+    free_blocks: np.ndarray | None = None  # physical ids not referenced by any table
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.context_lens.size else 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def kv_bytes_logical(self) -> int:
+        """K+V bytes one decode call reads, counting shared blocks once per reference."""
+        per_token = 2 * self.num_kv_heads * self.head_dim * ELEM_BYTES[self.dtype]
+        return int(self.context_lens.astype(np.int64).sum()) * per_token
+
+    def kv_bytes_unique(self) -> int:
+        """K+V bytes of the distinct live token slots (shared prefix counted once)."""
+        per_token = 2 * self.num_kv_heads * self.head_dim * ELEM_BYTES[self.dtype]
+        lens = self.context_lens.astype(np.int64)
+        shared = self.prefix_blocks * BLOCK_SIZE
+        if shared and len(lens):
+            return int(shared + (lens - shared).sum()) * per_token
+        return int(lens.sum()) * per_token
+
+    def algorithmic_bytes(self, unique: bool = False) -> int:
+        """KV + q + out + live block-table entries + context_lens."""
+        e = ELEM_BYTES[self.dtype]
+        qo = 2 * self.num_seqs * self.num_q_heads * self.head_dim * e
+        live_entries = int(((self.context_lens.astype(np.int64) + BLOCK_SIZE - 1) // BLOCK_SIZE).sum())
+        kv = self.kv_bytes_unique() if unique else self.kv_bytes_logical()
+        return kv + qo + 4 * live_entries + 4 * self.num_seqs
+
+
+def _scale_for(head_dim: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(head_dim)))
+
+
+def build_workload(
+    name: str,
+    rng: np.random.Generator,
+    *,
+    dtype: str,
+    num_q_heads: int,
+    num_kv_heads: int,
+    head_dim: int,
+    context_lens,
+    max_blocks_per_seq: int | None = None,
+    pool_blocks: int | None = None,
+    free_fraction: float = 0.10,
+    prefix_tokens: int = 0,
+    k_outlier_columns: int = 0,
+    outlier_gain: float = 10.0,
+    poison: bool = True,
+    tail_fill: str = "nan",
+    partition_size: int = 0,
+    scale: float | None = None,
+) -> Workload:
+    """Draw one workload.
+
+    Physical ids come from a seeded permutation of the pool and are handed out
+    in (sequence, logical block) order; shared prefix blocks are handed out
+    first.  With ``poison`` the blocks no table references are NaN, the slots
+    past a sequence's length inside its last block hold ``tail_fill``
+    ("nan" or "sentinel" = +-1e3), and table entries past the live range are -1.
+    """
+    lens = np.asarray(context_lens, dtype=np.int32)
+    B = len(lens)
+    if prefix_tokens % BLOCK_SIZE:
+        raise ValueError("shared prefix must be a whole number of blocks")
+    prefix_blocks = prefix_tokens // BLOCK_SIZE
+    need = [(int(L) + BLOCK_SIZE - 1) // BLOCK_SIZE for L in lens]
+    if max_blocks_per_seq is None:
+        max_blocks_per_seq = max(need) if need else 1
+    max_blocks_per_seq = max(max_blocks_per_seq, 1)
+    private = [n - prefix_blocks for n in need]
+    if prefix_blocks and min(private) < 0:
+        raise ValueError("every context must cover the shared prefix")
+    used = prefix_blocks + sum(private)
+    if pool_blocks is None:
+        pool_blocks = max(int(math.ceil(used * (1.0 + free_fraction))), used + 1)
+    if pool_blocks < used:
+        raise ValueError("pool too small")
+
+    perm = rng.permutation(pool_blocks).astype(np.int32)
+    tables = np.full((B, max_blocks_per_seq), -1, dtype=np.int32)
+    cursor = prefix_blocks
+    for s in range(B):
+        tables[s, :prefix_blocks] = perm[:prefix_blocks]
+        n = private[s]
+        tables[s, prefix_blocks:prefix_blocks + n] = perm[cursor:cursor + n]
+        cursor += n
+    free = perm[used:]
+
+    shape = (pool_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
+    k_pool = normal(rng, shape, dtype)
+    v_pool = normal(rng, shape, dtype)
+    if k_outlier_columns:
+        # a few (kv-head, channel) columns of K carry x10 values: the per-channel
+        # key outliers that motivate per-channel K quantisation on the pages
+        cols = rng.choice(num_kv_heads * head_dim, size=k_outlier_columns, replace=False)
+        for c in np.sort(cols):
+            g, ch = divmod(int(c), head_dim)
+            k_pool[:, g, :, ch] = normal(rng, (pool_blocks, BLOCK_SIZE), dtype, gain=outlier_gain)
+    q = normal(rng, (B, num_q_heads, head_dim), dtype)
+
+    if poison:
+        if len(free):
+            k_pool[free] = nan_fill((len(free),) + shape[1:], dtype)
+            v_pool[free] = nan_fill((len(free),) + shape[1:], dtype)
+        for s in range(B):
+            L = int(lens[s])
+            o = L % BLOCK_SIZE
+            if L == 0 or o == 0:
+                continue
+            b = tables[s, L // BLOCK_SIZE]
+            if tail_fill == "nan":
+                k_pool[b, :, o:, :] = nan_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype)
+                v_pool[b, :, o:, :] = nan_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype)
+            elif tail_fill == "sentinel":
+                k_pool[b, :, o:, :] = const_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype, 1e3)
+                v_pool[b, :, o:, :] = const_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype, -1e3)
+            else:
+                raise ValueError(tail_fill)
+
+    return Workload(
+        name=name, dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+        head_dim=head_dim, q=q, k_pool=k_pool, v_pool=v_pool, block_tables=tables,
+        context_lens=lens, scale=_scale_for(head_dim) if scale is None else float(np.float32(scale)),
+        partition_size=partition_size, prefix_blocks=prefix_blocks, free_blocks=free,
+    )
+
+
+# --------------------------------------------------------------------------
+# the five workload shapes
+# --------------------------------------------------------------------------
+CONFIG_NAMES = (
+    "tiny-mha-f32",          # B2, H4/4, d64, fp32, lens 17 and 40, pool of 8 blocks
+    "7b-mha-f16",            # B32, H32/32, d128, fp16, lens U[512, 4096]
+    "70b-gqa8-bf16-4k",      # B64, H64/8, d128, bf16, lens 4096, 1% x10 K channels
+    "shared-prefix-gqa4",    # B128, H32/8, d128, bf16, 1024 shared + U[16, 1024]
+    "long-32k-split512",     # B4, H64/8, d128, bf16, lens 32768, 512-token partitions
+)
+
+
+def make_config(index: int, seed: int | None = None, *, poison: bool = True,
+                tail_fill: str = "nan") -> Workload:
+    """Workload ``index`` (0..4) drawn with ``seed`` (default 1000 + index)."""
+    if seed is None:
+        seed = 1000 + index
+    rng = np.random.Generator(np.random.PCG64(seed))
+    name = CONFIG_NAMES[index]
+    kw = dict(poison=poison, tail_fill=tail_fill)
+    if index == 0:
+        return build_workload(name, rng, dtype="f32", num_q_heads=4, num_kv_heads=4,
+                              head_dim=64, context_lens=[17, 40], pool_blocks=8, **kw)
+    if index == 1:
+        lens = rng.integers(512, 4096, size=32, endpoint=True)
+        return build_workload(name, rng, dtype="f16", num_q_heads=32, num_kv_heads=32,
+                              head_dim=128, context_lens=lens, max_blocks_per_seq=256, **kw)
+    if index == 2:
+        return build_workload(name, rng, dtype="bf16", num_q_heads=64, num_kv_heads=8,
+                              head_dim=128, context_lens=[4096] * 64, max_blocks_per_seq=256,
+                              k_outlier_columns=10, **kw)
+    if index == 3:
+        lens = 1024 + rng.integers(16, 1024, size=128, endpoint=True)
+        return build_workload(name, rng, dtype="bf16", num_q_heads=32, num_kv_heads=8,
+                              head_dim=128, context_lens=lens, max_blocks_per_seq=128,
+                              prefix_tokens=1024, **kw)
+    if index == 4:
+        return build_workload(name, rng, dtype="bf16", num_q_heads=64, num_kv_heads=8,
+                              head_dim=128, context_lens=[32768] * 4, max_blocks_per_seq=2048,
+                              partition_size=512, **kw)
+    raise IndexError(index)
+
+
+def make_random_case(seed: int, *, num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                     head_dim: int, dtype: str, lens=None, max_len: int = 80,
+                     partition_size: int = 0, poison: bool = True, tail_fill: str = "nan",
+                     free_fraction: float = 0.25, prefix_tokens: int = 0) -> Workload:
+    """A small random case for parity sweeps (ragged lengths, several tiles)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if lens is None:
+        lens = rng.integers(max(prefix_tokens, 1), max_len, size=num_seqs, endpoint=True)
+    return build_workload(f"random-{seed}", rng, dtype=dtype, num_q_heads=num_q_heads,
+                          num_kv_heads=num_kv_heads, head_dim=head_dim, context_lens=lens,
+                          free_fraction=free_fraction, poison=poison, tail_fill=tail_fill,
+                          partition_size=partition_size, prefix_tokens=prefix_tokens)
