@@ -1,0 +1,254 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch: ``pa_decode`` (block
+table gather, logits, online softmax, P.V, GQA sharing, split-context
+partials) and, when the context is split, ``pa_reduce`` (log-sum-exp merge and
+store).  Inputs are resident in HBM before the timed region starts.
+
+Default workload: 70B-style GQA decode -- 64 sequences, 64 query heads over 8
+KV heads, head_dim 128, bf16 KV, every context 4096 tokens, 16-token blocks,
+shuffled block tables.  Prints one JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the decode kernel sources, to tell whether stored counters still apply."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_365_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, partition: int):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "pa_decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if entry.get("partition_size") != partition:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def decode_kernel_bytes(w) -> int:
+    """Algorithmic bytes one pa_decode launch must move: K and V rows of every live
+    token, q, live block-table entries and context lengths; plus the output rows
+    when it writes them itself (unsplit)."""
+    from paged_kv_cache_365_amd.workloads import ELEM_BYTES
+    e = ELEM_BYTES[w.dtype]
+    live = int(((w.context_lens.astype("int64") + 15) // 16).sum())
+    q = w.num_seqs * w.num_q_heads * w.head_dim * e
+    return w.kv_bytes_logical() + q + 4 * live + 4 * w.num_seqs
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_passes: int = 3):
+    """The fp64 oracle, single-threaded, on the same workload (bounded)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    B = w.num_seqs
+    # sample: whole sequences, up to `max_passes` passes over the workload or ~min_seconds
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        done_seqs = 0
+        passes = 0
+        while passes < max_passes:
+            for s in range(B):
+                oracle.paged_decode(w.q[s:s + 1], w.k_pool, w.v_pool, w.block_tables[s:s + 1],
+                                    w.context_lens[s:s + 1], w.scale, w.dtype)
+                done_seqs += 1
+                if time.perf_counter() - t0 > 3 * min_seconds:
+                    break
+            passes += 1
+            if time.perf_counter() - t0 >= min_seconds:
+                break
+        dt = time.perf_counter() - t0
+    frac = done_seqs / B
+    gbps = w.algorithmic_bytes() * frac / dt / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_seqs} sequences ({frac:.2f} passes over all {B} sequences x "
+                      f"{w.num_q_heads} heads of the workload), numpy float64, one thread, "
+                      f"{dt:.1f} s",
+            "tokens_per_s": round(done_seqs / dt, 3)}
+
+
+def copy_bandwidth(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Read+write GB/s of a plain device copy (context for the roofline)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del src, dst
+    return 2 * nbytes / dt / 1e9
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload index 0..4 (default: 70B GQA 4K)")
+    ap.add_argument("--partition", type=int, default=None, help="override the partition size")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              f"(the decode path is single-GPU; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_365_amd import pa, tuning
+    from paged_kv_cache_365_amd import workloads as wl
+    from paged_kv_cache_365_amd.device import upload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.load()
+
+    log(f"generating workload {args.config}")
+    w = wl.make_config(args.config, args.seed)
+    P = tuning.partition_for(w) if args.partition is None else args.partition
+    d = upload(w, "cuda")
+    out = torch.empty_like(d.q)
+    ws = pa.workspace_for(d.q, d.k_pool, d.max_context_len, P)
+    B, Hq, D = d.q.shape
+    stream = torch.cuda.current_stream()
+    log(f"{w.name}: B={B} Hq={Hq} Hkv={w.num_kv_heads} d={D} dtype={w.dtype} "
+        f"maxlen={w.max_context_len} partition={P}")
+
+    copy_gbps = None
+    if args.copy_calibration:
+        copy_gbps = copy_bandwidth(torch)
+        log(f"device copy: {copy_gbps:.0f} GB/s (read+write)")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if P:
+            pa.pa_decode(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                         d.max_context_len, d.scale, P, ws, None, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            pa.pa_reduce(ws, d.context_lens, B, Hq, D, d.max_context_len, P, out, stream)
+        else:
+            pa.pa_decode(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                         d.max_context_len, d.scale, 0, None, out, stream)
+            if ev is not None:
+                ev[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms")
+
+    decode_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    reduce_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events])) if P else 0.0
+    ms_per_step = wall * 1e3 / args.steps
+    alg = w.algorithmic_bytes()
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    kbytes = decode_kernel_bytes(w)
+    achieved = kbytes / (decode_ms * 1e-3) / 1e9
+    traffic = stored_traffic(w.name, P)
+
+    rec = {
+        "metric": "paged decode-attention KV GB/s and % of HBM peak; tokens/s at 70B-GQA 4K",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "accum_dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
+            "head_dim": D, "max_context_len": w.max_context_len, "block_size": 16,
+            "partition_size": P, "pool_blocks": w.num_blocks, "seed": args.seed if args.seed is not None else 1000 + args.config,
+        },
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": alg,
+        "decode_us": round(decode_ms * 1e3, 2),
+        "reduce_us": round(reduce_ms * 1e3, 2),
+        "roofline": {
+            "kernel": "pa_decode",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kbytes,
+        },
+    }
+    if copy_gbps is not None:
+        rec["device_copy_gbps"] = round(copy_gbps, 1)
+    del d, out, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host (cpu_baseline)")
+        rec["cpu_baseline"] = cpu_baseline(w)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,150 @@
+/*
+ * pa.h -- single-token decode attention over a paged KV cache, for MI355X (gfx950).
+ *
+ * The method: K and V of every cached token live in a shared pool of fixed-size
+ * physical blocks of 16 tokens; a per-sequence block table maps logical block i
+ * (tokens 16i .. 16i+15) to a physical block; blocks are taken from the pool
+ * when they are written and several tables may point at the same physical block
+ * (a shared prompt prefix).  See the pages
+ *   "LLM 推理优化：KV Cache、PagedAttention 与量化" (blog.tanteng.space), §2.2, §2.3
+ *   "大模型推理加速与显存黑科技 (Inference Acceleration & KV Cache)" (ialgorithm.me),
+ *     §2 (attention equation), §3.2 (block-table figure), §4.2 (online softmax)
+ *   "大模型推理加速：从 KV Cache 到投机采样的工程实践" (ybb.press), "主流优化策略" (GQA/MQA)
+ *   "LLM推理优化实战：从KV Cache到Speculative Decoding，把延迟打下来" (jsqmd.com),
+ *     KVCacheAttention listing (scale d^-0.5; new K/V appended before attending).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - All pointers except `pool` descriptors are DEVICE pointers owned by the
+ *    caller.  The library allocates no device memory, keeps no state between
+ *    calls and is reentrant.
+ *  - Every call is asynchronous on `stream` (NULL = the null stream) and never
+ *    synchronises.  Argument errors are reported synchronously by the return
+ *    value and nothing is launched; PA_ERR_HIP reports a failed launch.
+ *  - Element dtype: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16), PA_BF16
+ *    (bfloat16).  q, out, the pools and new K/V rows share the pool dtype.
+ *  - KV pool layout: k_pool and v_pool are each [num_blocks][num_kv_heads][16][head_dim],
+ *    dense, row-major.  One (physical block, kv head) tile of 16 token rows is
+ *    contiguous (4 KiB for head_dim 128 in a 16-bit dtype).  Token slot
+ *    = physical_block * 16 + offset.
+ *  - Block tables: int32 [num_seqs][max_blocks_per_seq], row-major.  Entry j of
+ *    row s is the physical block of tokens 16j .. 16j+15 of sequence s.  Only
+ *    the first ceil(context_lens[s] / 16) entries of a row are read.
+ *  - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads)
+ *    (contiguous groups; num_q_heads == num_kv_heads is MHA, num_kv_heads == 1 MQA).
+ *  - Device-side data are not validated (that would need a synchronisation):
+ *    a physical id outside [0, num_blocks) is clamped into range and a context
+ *    length is clamped into [0, max_context_len], so a bad table yields a wrong
+ *    result but never an out-of-bounds access.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad head ratio, ... */
+  PA_ERR_UNSUPPORTED = -2, /* dtype, head_dim or block_size outside what is built */
+  PA_ERR_MISALIGNED = -3,  /* a device pointer is not 16-byte aligned */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+  PA_ERR_HIP = -5          /* a kernel launch failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Host-side description of a KV pool.  block_size must be 16 and head_dim 64
+ * or 128. */
+typedef struct pa_pool_desc {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* a pa_dtype value */
+} pa_pool_desc;
+
+/* Fill every element of both pools: fill = 0 writes +0.0, fill = 1 writes a
+ * quiet NaN (used to prove that unreferenced blocks are never read).  A pool
+ * that has just been taken from the allocator (the fixed-capacity block pool of
+ * §2.3 of the tanteng.space page). */
+pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int32_t fill,
+                       hipStream_t stream);
+
+/* KV append: for each of num_tokens new tokens i, copy k_new[i] and v_new[i]
+ * ([num_kv_heads][head_dim] each, pool dtype, so k_new is [num_tokens][H_kv][d])
+ * bit for bit into slot slot_mapping[i] = physical * 16 + offset of both pools.
+ * A negative slot skips the token; slots >= num_blocks * 16 are also skipped.
+ * Two tokens with the same slot race (the caller's contract).  This is the step
+ * that puts the new token's K/V into the cache before attention, as the
+ * KVCacheAttention listing of the jsqmd.com page does with its concatenation. */
+pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                      hipStream_t stream);
+
+/* Bytes of workspace pa_decode needs for split-context partials: float32
+ * o_part[num_seqs][num_q_heads][n_parts][head_dim] followed by float32
+ * lse_part[num_seqs][num_q_heads][n_parts], n_parts = ceil(max_context_len /
+ * partition_size).  0 when partition_size is 0 (single phase) and on bad
+ * arguments. */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/* Decode attention for one query token per sequence:
+ *   out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
+ * over the context_lens[s] tokens the block table of s addresses (the equation
+ * of §2 of the ialgorithm.me page; the gather of its §3.2 figure).  q and out
+ * are [num_seqs][num_q_heads][head_dim] in the pool dtype; out is rounded to
+ * nearest-even from float32 accumulators.  A zero-length context gives a zero
+ * row.
+ *
+ * partition_size == 0: single phase, out is written.
+ * partition_size  > 0 (a multiple of 16): the context of each sequence is cut
+ *   into partitions of partition_size tokens; partition p of (s, h) writes
+ *   o_part = its own normalised attention output and lse_part = ln sum exp of
+ *   its logits (-inf and a zero row for an empty partition) into `workspace`
+ *   (layout: pa_decode_workspace_bytes); `out` is not touched and may be NULL.
+ *   pa_reduce then merges the partials into out.
+ * max_context_len bounds every context length and must not exceed
+ * 16 * max_blocks_per_seq. */
+pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* out, hipStream_t stream);
+
+/* Log-sum-exp merge of the partials pa_decode wrote into `workspace` (same
+ * num_seqs, num_q_heads, head_dim, max_context_len and partition_size):
+ *   M = max_p lse_p,  LSE = M + ln sum_p exp(lse_p - M),
+ *   out[s][h] = sum_p exp(lse_p - LSE) o_p,
+ * over the ceil(context_lens[s] / partition_size) partitions sequence s has.
+ * Exact because the softmax normaliser can be streamed (§4.2 of the
+ * ialgorithm.me page).  out is [num_seqs][num_q_heads][head_dim] in out_dtype. */
+pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                    int32_t partition_size, int32_t out_dtype, void* out, hipStream_t stream);
+
+/* The gather indices pa_decode uses, computed by the same device function:
+ * slot_ids[s][t] = block_tables[s][t / 16] * 16 + t % 16 for t < context_lens[s]
+ * (after the same clamping), -1 for context_lens[s] <= t < max_context_len.
+ * slot_ids is int64 [num_seqs][max_context_len].  Used to check the block-table
+ * arithmetic bit for bit (the worked example of §3.2 of the ialgorithm.me page).
+ * num_blocks is the pool size used for clamping. */
+pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t num_blocks, int64_t* slot_ids,
+                            hipStream_t stream);
+
+/* Static, NUL-terminated name of a status code. */
+const char* pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,75 @@
+"""Build ``libpa.so`` (the HIP library behind ``include/pa.h``) for gfx950.
+
+``python -m paged_kv_cache_365_amd.build`` compiles every ``csrc/*.hip`` with
+hipcc into ``paged_kv_cache_365_amd/libpa.so`` (in-tree, so the library travels
+with the source tree).  Always recompiles.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libpa.so")
+ARCH = "gfx950"
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Wall", "-Wno-unused-function",
+    # no packed-FP32 (v_pk_*_f32) instructions anywhere in the library
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; ROCm is required to build libpa.so")
+    return path
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile and link libpa.so; returns its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="pa_build_") as tmp:
+        objs, procs = [], []
+        for src in sources():
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+            if len([p for _, p in procs if p.poll() is None]) >= jobs:
+                procs[0][1].wait()
+        for src, p in procs:
+            out, _ = p.communicate()
+            text = "\n".join(line for line in out.splitlines()
+                             if "is not a recognized feature for this target" not in line)
+            if p.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{text}")
+            if verbose and text.strip():
+                print(text)
+        tmp_lib = LIB + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp_lib, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

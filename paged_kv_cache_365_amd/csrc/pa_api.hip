@@ -1,0 +1,210 @@
+// C-ABI front end: argument validation, workspace sizing, kernel selection.
+// Nothing here allocates device memory or synchronises.
+#include <limits.h>
+
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
+}
+
+namespace {
+
+constexpr int kMaxReduceParts = 16384;  // partition weights staged in 64 KiB of LDS
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16:
+    case PA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+pa_status check_pool(const pa_pool_desc* pool) {
+  if (!pool) return PA_ERR_INVALID_ARG;
+  if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
+  if (pool->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (elem_bytes(pool->dtype) == 0) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+size_t pool_bytes(const pa_pool_desc* pool) {
+  return static_cast<size_t>(pool->num_blocks) * pool->num_kv_heads * pa::kBlockSize *
+         pool->head_dim * elem_bytes(pool->dtype);
+}
+
+int32_t num_parts_for(int32_t max_context_len, int32_t partition_size) {
+  const int64_t n = (static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+  return static_cast<int32_t>(n < 1 ? 1 : n);
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_MISALIGNED: return "PA_ERR_MISALIGNED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int32_t fill,
+                       hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (!k_pool || !v_pool || (fill != 0 && fill != 1)) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return PA_ERR_MISALIGNED;
+  uint32_t pattern = 0u;
+  if (fill == 1) {
+    pattern = pool->dtype == PA_F32 ? 0x7FC00000u : (pool->dtype == PA_F16 ? 0x7E007E00u : 0x7FC07FC0u);
+  }
+  const size_t bytes = pool_bytes(pool);
+  hipError_t e = pa::launch_fill(k_pool, bytes, pattern, stream);
+  if (e == hipSuccess) e = pa::launch_fill(v_pool, bytes, pattern, stream);
+  return from_hip(e);
+}
+
+pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                      hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(slot_mapping, 8))
+    return PA_ERR_MISALIGNED;
+  const int row_bytes = pool->head_dim * elem_bytes(pool->dtype);
+  return from_hip(pa::launch_write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
+                                      pool->num_blocks, pool->num_kv_heads, row_bytes, stream));
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0)
+    return 0;
+  const size_t parts = static_cast<size_t>(num_parts_for(max_context_len, partition_size));
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * parts;
+  return rows * head_dim * sizeof(float) + rows * sizeof(float);
+}
+
+pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* out, hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * pa::kBlockSize)
+    return PA_ERR_INVALID_ARG;
+  if (partition_size < 0 || partition_size % pa::kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;  // grid z
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4))
+    return PA_ERR_MISALIGNED;
+
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.num_blocks = pool->num_blocks;
+  a.max_context_len = max_context_len;
+  a.dtype = pool->dtype;
+  a.scale = scale;
+
+  if (partition_size == 0) {
+    if (!out) return PA_ERR_INVALID_ARG;
+    if (!aligned(out, 16)) return PA_ERR_MISALIGNED;
+    // one partition spanning every context
+    const int64_t span = (static_cast<int64_t>(max_context_len) + pa::kBlockSize - 1) /
+                         pa::kBlockSize * pa::kBlockSize;
+    a.partition_tokens = static_cast<int32_t>(span < pa::kBlockSize ? pa::kBlockSize : span);
+    a.num_parts = 1;
+    a.write_partials = false;
+    a.out = out;
+  } else {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
+                                                  max_context_len, partition_size);
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
+    a.partition_tokens = partition_size;
+    a.num_parts = num_parts_for(max_context_len, partition_size);
+    a.write_partials = true;
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * a.num_parts;
+    a.o_part = static_cast<float*>(workspace);
+    a.lse_part = a.o_part + rows * pool->head_dim;
+  }
+  return from_hip(pa::launch_decode_valu(a, stream));
+}
+
+pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                    int32_t partition_size, int32_t out_dtype, void* out, hipStream_t stream) {
+  if (!workspace || !context_lens || !out) return PA_ERR_INVALID_ARG;
+  if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
+  if (partition_size <= 0 || partition_size % pa::kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (elem_bytes(out_dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  if (!aligned(workspace, 16) || !aligned(out, 16) || !aligned(context_lens, 4))
+    return PA_ERR_MISALIGNED;
+  pa::ReduceArgs a{};
+  a.num_parts = num_parts_for(max_context_len, partition_size);
+  if (a.num_parts > kMaxReduceParts) return PA_ERR_UNSUPPORTED;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * a.num_parts;
+  a.o_part = static_cast<const float*>(workspace);
+  a.lse_part = a.o_part + rows * head_dim;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  a.max_context_len = max_context_len;
+  a.partition_tokens = partition_size;
+  a.dtype = out_dtype;
+  a.out = out;
+  return from_hip(pa::launch_reduce(a, stream));
+}
+
+pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs,
+                            int32_t max_context_len, int32_t num_blocks, int64_t* slot_ids,
+                            hipStream_t stream) {
+  if (!block_tables || !context_lens || !slot_ids) return PA_ERR_INVALID_ARG;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * pa::kBlockSize)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(slot_ids, 8))
+    return PA_ERR_MISALIGNED;
+  if (max_context_len == 0) return PA_OK;
+  return from_hip(pa::launch_slot_ids(block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                      max_context_len, num_blocks, slot_ids, stream));
+}
+
+}  // extern "C"

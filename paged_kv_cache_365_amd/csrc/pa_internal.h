@@ -1,0 +1,65 @@
+// Host-side launch interfaces between the C-ABI front end (pa_api.hip) and the
+// kernel translation units.  Arguments are validated by the front end before
+// any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_blocks;
+  int32_t max_context_len;
+  int32_t dtype;
+  float scale;
+  int32_t partition_tokens;  // tokens per partition (a multiple of 16)
+  int32_t num_parts;         // partitions per sequence in the grid
+  bool write_partials;       // true: o_part/lse_part into the workspace; false: out
+  float* o_part;
+  float* lse_part;
+  void* out;
+};
+
+// Launch the decode kernel chosen for (dtype, head_dim, group size).
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct ReduceArgs {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t max_context_len;
+  int32_t partition_tokens;
+  int32_t num_parts;
+  int32_t dtype;
+  void* out;
+};
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
+
+hipError_t launch_fill(void* dst, size_t bytes16, uint32_t pattern, hipStream_t stream);
+
+hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                           int32_t num_kv_heads, int32_t row_bytes, hipStream_t stream);
+
+hipError_t launch_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                           int32_t num_blocks, int64_t* slot_ids, hipStream_t stream);
+
+}  // namespace pa
