@@ -84,19 +84,40 @@ def slot_ids(block_tables: np.ndarray, context_lens: np.ndarray, max_context_len
 
 def tile_byte_offset(physical: int, kv_head: int, num_kv_heads: int, head_dim: int,
                      elem_bytes: int) -> int:
-    """Byte offset of tile (physical block, kv head) in a pool laid out as
-    [num_blocks][H_kv][16][d]: tiles are 16 * d * elem_bytes bytes each and are
-    ordered block-major, then by KV head."""
+    """Byte offset of tile (physical block, kv head) in a pool of 16 * d-element
+    tiles ordered block-major, then by KV head."""
     tile_bytes = BLOCK_SIZE * head_dim * elem_bytes
     return (physical * num_kv_heads + kv_head) * tile_bytes
 
 
-def gather_context(pool: np.ndarray, table_row: np.ndarray, length: int, kv_head: int) -> np.ndarray:
-    """Rows [length][d] (stored dtype) of one KV head of one sequence, in token order:
-    row t comes from physical block table_row[t // 16] at offset t % 16."""
+# Pool layouts (the library's ABI; only the order of elements inside a tile
+# differs between K and V):
+#   K  [blocks][H_kv][d / x][16][x]   x = elements per 16-byte chunk: element c
+#                                      of the token at offset o is at [c // x][o][c % x]
+#   V  [blocks][H_kv][d][16]          element c of the token at offset o is at [c][o]
+def k_rows(k_pool: np.ndarray, table_row: np.ndarray, length: int, kv_head: int) -> np.ndarray:
+    """K rows [length][d] (stored dtype) of one KV head of one sequence, in token
+    order: row t comes from physical block table_row[t // 16] at offset t % 16."""
     t = np.arange(length)
     physical = table_row[t // BLOCK_SIZE]
-    return pool[physical, kv_head, t % BLOCK_SIZE, :]
+    offset = t % BLOCK_SIZE
+    n_chunks, x = k_pool.shape[2], k_pool.shape[4]
+    rows = np.empty((length, n_chunks, x), dtype=k_pool.dtype)
+    for c in range(n_chunks):
+        rows[:, c, :] = k_pool[physical, kv_head, c, offset, :]
+    return rows.reshape(length, n_chunks * x)
+
+
+def v_rows(v_pool: np.ndarray, table_row: np.ndarray, length: int, kv_head: int) -> np.ndarray:
+    """V rows [length][d] (stored dtype), in token order, from the [d][16] tiles."""
+    t = np.arange(length)
+    physical = table_row[t // BLOCK_SIZE]
+    offset = t % BLOCK_SIZE
+    d = v_pool.shape[2]
+    rows = np.empty((length, d), dtype=v_pool.dtype)
+    for c in range(d):
+        rows[:, c] = v_pool[physical, kv_head, c, offset]
+    return rows
 
 
 # --------------------------------------------------------------------------
@@ -146,8 +167,8 @@ def paged_decode(q, k_pool, v_pool, block_tables, context_lens, scale, dtype,
         by_head.setdefault((s, _gqa_kv_head(h, Hq, Hkv)), []).append(h)
     for (s, g), heads in by_head.items():
         L = int(context_lens[s])
-        K = widen(gather_context(k_pool, block_tables[s], L, g), dtype)
-        V = widen(gather_context(v_pool, block_tables[s], L, g), dtype)
+        K = widen(k_rows(k_pool, block_tables[s], L, g), dtype)
+        V = widen(v_rows(v_pool, block_tables[s], L, g), dtype)
         for h in heads:
             out[s, h], _ = attend_range(widen(q[s, h], dtype), K, V, scale64)
     return out
@@ -176,8 +197,8 @@ def paged_decode_partials(q, k_pool, v_pool, block_tables, context_lens, scale, 
     for s in range(B):
         L = int(context_lens[s])
         for g in range(Hkv):
-            K = widen(gather_context(k_pool, block_tables[s], L, g), dtype)
-            V = widen(gather_context(v_pool, block_tables[s], L, g), dtype)
+            K = widen(k_rows(k_pool, block_tables[s], L, g), dtype)
+            V = widen(v_rows(v_pool, block_tables[s], L, g), dtype)
             for h in range(g * (Hq // Hkv), (g + 1) * (Hq // Hkv)):
                 qv = widen(q[s, h], dtype)
                 for p in range(P):
@@ -218,14 +239,17 @@ def write_kv(k_pool, v_pool, k_new, v_new, slot_mapping):
     """Copies of the pools with token i's [H_kv][d] rows stored at slot_mapping[i].
 
     A slot is physical * 16 + offset; negative slots are skipped.  Values are
-    copied bit for bit.
+    copied bit for bit into the K and V tile layouts described above.
     """
     k_out = k_pool.copy()
     v_out = v_pool.copy()
+    n_kv, n_chunks, x = k_pool.shape[1], k_pool.shape[2], k_pool.shape[4]
     for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
         if slot < 0:
             continue
         b, o = divmod(int(slot), BLOCK_SIZE)
-        k_out[b, :, o, :] = k_new[i]
-        v_out[b, :, o, :] = v_new[i]
+        for g in range(n_kv):
+            for c in range(n_chunks * x):
+                k_out[b, g, c // x, o, c % x] = k_new[i, g, c]
+                v_out[b, g, c, o] = v_new[i, g, c]
     return k_out, v_out

@@ -5,10 +5,6 @@
 #include "pa_common.h"
 #include "pa_internal.h"
 
-namespace pa {
-hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
-}
-
 namespace {
 
 constexpr int kMaxReduceParts = 16384;  // partition weights staged in 64 KiB of LDS
@@ -90,7 +86,8 @@ pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, cons
     return PA_ERR_MISALIGNED;
   const int row_bytes = pool->head_dim * elem_bytes(pool->dtype);
   return from_hip(pa::launch_write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
-                                      pool->num_blocks, pool->num_kv_heads, row_bytes, stream));
+                                      pool->num_blocks, pool->num_kv_heads, row_bytes,
+                                      elem_bytes(pool->dtype), stream));
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -160,7 +157,7 @@ pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
     a.o_part = static_cast<float*>(workspace);
     a.lse_part = a.o_part + rows * pool->head_dim;
   }
-  return from_hip(pa::launch_decode_valu(a, stream));
+  return from_hip(pa::launch_decode(a, stream));
 }
 
 pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,

@@ -63,16 +63,21 @@ __global__ __launch_bounds__(256) void fill_kernel(uint4* dst, size_t n16, uint3
 }
 
 // ---------------------------------------------------------------------------
-// write_kv: token i's [H_kv][row] K and V rows go to slot slot_mapping[i];
-// one thread per 16-byte chunk, a plain copy of bits.
+// write_kv: token i's [H_kv][d] K and V rows go to slot slot_mapping[i]; one
+// thread per 16-byte chunk of an input row, a plain copy of bits into the tile
+// layouts: K tiles are [d / x][16][x] (the chunk lands whole at (chunk, offset)),
+// V tiles are [d][16] (the chunk's x elements land in x different columns).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void write_kv_kernel(uint4* k_pool, uint4* v_pool,
+template <typename E>
+__global__ __launch_bounds__(256) void write_kv_kernel(char* k_pool, char* v_pool,
                                                        const uint4* k_new, const uint4* v_new,
                                                        const int64_t* slot_mapping, int num_tokens,
                                                        int64_t num_slots, int num_kv_heads,
                                                        int chunks_per_row) {
+  constexpr int kX = 16 / sizeof(E);  // elements per chunk
   const int chunks_per_token = num_kv_heads * chunks_per_row;
   const int64_t total = static_cast<int64_t>(num_tokens) * chunks_per_token;
+  const size_t tile_bytes = static_cast<size_t>(kBlockSize) * chunks_per_row * 16;
   for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int tok = static_cast<int>(idx / chunks_per_token);
@@ -80,13 +85,17 @@ __global__ __launch_bounds__(256) void write_kv_kernel(uint4* k_pool, uint4* v_p
     if (slot < 0 || slot >= num_slots) continue;
     const int rem = static_cast<int>(idx % chunks_per_token);
     const int g = rem / chunks_per_row;
-    const int c = rem % chunks_per_row;
+    const int ch = rem % chunks_per_row;
     const int64_t phys = slot / kBlockSize;
     const int o = static_cast<int>(slot % kBlockSize);
-    const size_t dst = ((static_cast<size_t>(phys) * num_kv_heads + g) * kBlockSize + o) *
-                           chunks_per_row + c;
-    k_pool[dst] = k_new[idx];
-    v_pool[dst] = v_new[idx];
+    const size_t tile = (static_cast<size_t>(phys) * num_kv_heads + g) * tile_bytes;
+    *reinterpret_cast<uint4*>(k_pool + tile + (static_cast<size_t>(ch) * kBlockSize + o) * 16) = k_new[idx];
+    const uint4 v = v_new[idx];
+    E e[kX];
+    __builtin_memcpy(e, &v, 16);
+    E* vt = reinterpret_cast<E*>(v_pool + tile);
+#pragma unroll
+    for (int i = 0; i < kX; ++i) vt[(ch * kX + i) * kBlockSize + o] = e[i];
   }
 }
 
@@ -137,11 +146,13 @@ hipError_t launch_fill(void* dst, size_t bytes, uint32_t pattern, hipStream_t st
 
 hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                           int32_t num_kv_heads, int32_t row_bytes, hipStream_t stream) {
+                           int32_t num_kv_heads, int32_t row_bytes, int32_t elem_bytes,
+                           hipStream_t stream) {
   const int chunks_per_row = row_bytes / 16;
   const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * chunks_per_row;
-  hipLaunchKernelGGL(write_kv_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
-                     static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool),
+  auto kernel = elem_bytes == 4 ? write_kv_kernel<uint32_t> : write_kv_kernel<uint16_t>;
+  hipLaunchKernelGGL(kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
+                     static_cast<char*>(k_pool), static_cast<char*>(v_pool),
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
                      slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * kBlockSize,
                      num_kv_heads, chunks_per_row);

@@ -1,0 +1,350 @@
+// Paged decode attention on the matrix cores (gfx950), all element types.
+//
+// Work unit.  A workgroup of kWaves wavefronts owns (sequence s, KV head g, a
+// chunk of up to 16 query heads of g's group, partition p).  The partition's
+// 16-token blocks are dealt round-robin to the waves; every wave streams its
+// blocks through registers, keeping the next block's K and V in flight while
+// the current one is consumed, and carries its own online-softmax state.  The
+// waves are merged at the end through LDS with the log-sum-exp algebra, in a
+// fixed order (no atomics: runs are bit-reproducible).
+//
+// Per 16-token block, everything is two small matrix products whose operands
+// come straight from the loads (lane l: r = l % 16, q = l / 16):
+//
+//   logits  S^T[token][head] = K[token][:] . Q[head][:]        (16 x 16 x d)
+//           A = K tile: the pool stores K chunk-major ([d/x][16][x], x elements
+//               per 16 bytes), so load j of a tile is the contiguous 1 KiB
+//               tile[64 j + lane] = chunk 4j + q of token r: exactly lane l's
+//               A operand of step j.
+//           B = Q: lane l holds chunk 4j + q of query head r (zero rows pad the
+//               group to 16).
+//           out: lane l holds the logits of tokens 4q .. 4q+3 for head r.
+//   P.V     O^T[col][head] += V^T[col][token] . P^T[token][head]   (16 x 16 x 16 per 16 columns)
+//           A = V tile: the pool stores V head-dim-major ([d][16]), so lane l's
+//               operand (tokens 4q .. 4q+3 of column 16 cb + r) is one
+//               contiguous 4-element load, and the 64 lanes read 64 * 4
+//               contiguous elements.
+//           B = P: lane l already holds the weights of tokens 4q .. 4q+3 for
+//               head r -- the logits' own output layout -- so P never moves.
+//           out: lane l holds O[head r][16 cb + 4q .. 16 cb + 4q + 3].
+//
+// Online softmax (§4.2 of the ialgorithm.me page: the normaliser is updated
+// while streaming, exactly): the running maximum m of each head is shared by
+// the four lanes holding that head (two lane-swap max steps per block).  m is
+// only raised when a block's maximum exceeds it by more than kSlack (log2
+// units); until then weights up to 2^kSlack are accumulated as they are.  The
+// result is the same algebra (every partial sum uses one common reference), and
+// the rescale of the accumulators becomes rare.  Weights are rounded to the KV
+// element type for the matrix product and the running sum adds exactly the
+// rounded values, so out is a true convex combination of V rows.
+//
+// Partial blocks: the rows past the context end of a block may hold anything
+// (NaN included); their logits are selected to -inf and their V elements to 0
+// before any arithmetic touches them.
+#include "pa_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kSlack = 8.0f;  // log2 headroom before the running maximum is raised
+
+// ---------------------------------------------------------------------------
+// element-type specific operand handling
+// ---------------------------------------------------------------------------
+struct MmaBF16 {
+  static constexpr int kBytes = 2;
+  using VLoad = uint2;  // 4 tokens of one V column
+  using POp = uint2;    // 4 weights
+  // one 16-byte chunk per lane = one 16x16x32 step
+  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4& q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v),
+                                                     __builtin_bit_cast(s16x4, p), c, 0, 0, 0);
+  }
+  // round the weights (nearest even) and return the sum of the rounded values
+  static __device__ __forceinline__ POp pack(const float (&p)[4], float& sum) {
+    const bf16x2 a = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1])};
+    const bf16x2 b = {static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a);
+    const uint32_t ub = __builtin_bit_cast(uint32_t, b);
+    sum += (__uint_as_float(ua << 16) + __uint_as_float(ua & 0xffff0000u)) +
+           (__uint_as_float(ub << 16) + __uint_as_float(ub & 0xffff0000u));
+    return make_uint2(ua, ub);
+  }
+  // keep the first n (0..4) tokens of a V load, zero the rest
+  static __device__ __forceinline__ void keep(VLoad& v, int n) {
+    const uint64_t bits = n >= 4 ? ~0ull : ((1ull << (16 * n)) - 1ull);
+    v.x &= static_cast<uint32_t>(bits);
+    v.y &= static_cast<uint32_t>(bits >> 32);
+  }
+};
+
+struct MmaF16 {
+  static constexpr int kBytes = 2;
+  using VLoad = uint2;
+  using POp = uint2;
+  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4& q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
+                                                 __builtin_bit_cast(f16x4, p), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ POp pack(const float (&p)[4], float& sum) {
+    const f16x2 a = {static_cast<_Float16>(p[0]), static_cast<_Float16>(p[1])};
+    const f16x2 b = {static_cast<_Float16>(p[2]), static_cast<_Float16>(p[3])};
+    sum += (static_cast<float>(a[0]) + static_cast<float>(a[1])) +
+           (static_cast<float>(b[0]) + static_cast<float>(b[1]));
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+  }
+  static __device__ __forceinline__ void keep(VLoad& v, int n) { MmaBF16::keep(v, n); }
+};
+
+struct MmaF32 {
+  static constexpr int kBytes = 4;
+  using VLoad = uint4;  // 4 tokens of one V column
+  struct POp {
+    float p[4];
+  };
+  // a 16-byte chunk holds 4 elements: four 16x16x4 steps, element e of every
+  // lane's chunk forming step e
+  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4& q, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.x), __uint_as_float(q.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.y), __uint_as_float(q.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.z), __uint_as_float(q.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w), __uint_as_float(q.w), c, 0, 0, 0);
+    return c;
+  }
+  // token 4q + e of the lane's V load meets weight e: step e pairs them
+  static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.x), p.p[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.y), p.p[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.z), p.p[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w), p.p[3], c, 0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ POp pack(const float (&p)[4], float& sum) {
+    sum += (p[0] + p[1]) + (p[2] + p[3]);
+    return POp{{p[0], p[1], p[2], p[3]}};
+  }
+  static __device__ __forceinline__ void keep(VLoad& v, int n) {
+    if (n < 1) v.x = 0u;
+    if (n < 2) v.y = 0u;
+    if (n < 3) v.z = 0u;
+    if (n < 4) v.w = 0u;
+  }
+};
+
+// maximum / sum over the four lanes r, r+16, r+32, r+48 (lane-swap butterflies)
+__device__ __forceinline__ float max_over_q(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_q(float v) {
+  const uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t w = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <class M, class Tr, int D, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
+  constexpr int kKLoads = D * M::kBytes / 64;  // 1 KiB K loads per tile (= 16-byte chunks / 4)
+  constexpr int kColBlocks = D / 16;           // P.V output blocks of 16 columns
+  constexpr int kPad = 4;                      // LDS row padding (floats)
+  using VLoad = typename M::VLoad;
+
+  __shared__ float sm_o[kWaves][16][D + kPad];
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
+
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int qg = lane >> 4;
+  const int wave = wave_id();
+  const int part = blockIdx.x;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int chunks = (group + 15) / 16;
+  const int g = blockIdx.y / chunks;
+  const int hc = blockIdx.y % chunks;
+  const int h0 = g * group + hc * 16;
+  const int nh = min(16, group - hc * 16);  // live query heads in this chunk
+  const int s = blockIdx.z;
+
+  const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
+  const int t_lo = part * a.partition_tokens;
+  const int t_hi = min(L, t_lo + a.partition_tokens);
+  const int blk_lo = t_lo / kBlockSize;
+  const int blk_hi = t_hi > t_lo ? (t_hi + kBlockSize - 1) / kBlockSize : blk_lo;
+
+  // B operand of the logits: chunk 4j + qg of query head h0 + r (zero padding rows)
+  uint4 qop[kKLoads];
+  {
+    const int hq = h0 + min(r, nh - 1);  // padding rows read a live row, then drop it
+    const char* qrow = static_cast<const char*>(a.q) +
+                       (static_cast<size_t>(s) * a.num_q_heads + hq) * D * M::kBytes;
+#pragma unroll
+    for (int j = 0; j < kKLoads; ++j) {
+      const uint4 v = reinterpret_cast<const uint4*>(qrow)[4 * j + qg];
+      qop[j] = r < nh ? v : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  const float qs = a.scale * kLog2e;  // logits in log2 units
+
+  float m = -INFINITY;  // running maximum (log2 units) of head r, shared by its 4 lanes
+  float lsum = 0.f;     // this lane's share of the running sum
+  f32x4 acc[kColBlocks];
+#pragma unroll
+  for (int cb = 0; cb < kColBlocks; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int32_t* __restrict__ trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
+  const char* __restrict__ kbase = static_cast<const char*>(a.k_pool);
+  const char* __restrict__ vbase = static_cast<const char*>(a.v_pool);
+
+  auto load = [&](int jb, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
+    const int phys = pa_physical_block(trow, jb, a.num_blocks);
+    const size_t tile = pa_tile_offset(phys, g, a.num_kv_heads, D) * M::kBytes;
+    const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
+    const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + tile);
+#pragma unroll
+    for (int j = 0; j < kKLoads; ++j) kr[j] = kt[64 * j + lane];
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = vt[(16 * cb + r) * 4 + qg];
+  };
+
+  auto consume = [&](int jb, const uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kKLoads; ++j) sc = M::qk(kr[j], qop[j], sc);
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs;
+    const int tok0 = jb * kBlockSize + 4 * qg;  // first token of this lane's four
+    if ((jb + 1) * kBlockSize > t_hi) {          // partial block (wave-uniform test)
+      const int n = min(max(t_hi - tok0, 0), 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (i >= n) x[i] = -INFINITY;
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) M::keep(vr[cb], n);
+    }
+    const float bmax = max_over_q(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const bool raise = bmax > m + kSlack;
+    if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform
+      const float mn = raise ? bmax : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block, 1 if kept
+      m = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) acc[cb] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m);
+    const typename M::POp pop = M::pack(p, lsum);
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb) acc[cb] = M::pv(vr[cb], pop, acc[cb]);
+  };
+
+  // two register sets: block jb is consumed while block jb + kWaves is loading
+  uint4 ka[kKLoads], kb[kKLoads];
+  VLoad va[kColBlocks], vb[kColBlocks];
+  int jb = blk_lo + wave;
+  if (jb < blk_hi) load(jb, ka, va);
+  while (jb < blk_hi) {
+    int jn = jb + kWaves;
+    if (jn < blk_hi) load(jn, kb, vb);
+    consume(jb, ka, va);
+    jb = jn;
+    if (jb >= blk_hi) break;
+    jn = jb + kWaves;
+    if (jn < blk_hi) load(jn, ka, va);
+    consume(jb, kb, vb);
+    jb = jn;
+  }
+
+  // this wave's results -> LDS
+  lsum = sum_over_q(lsum);
+#pragma unroll
+  for (int cb = 0; cb < kColBlocks; ++cb)
+    *reinterpret_cast<f32x4*>(&sm_o[wave][r][16 * cb + 4 * qg]) = acc[cb];
+  if (qg == 0) {
+    sm_m[wave][r] = m;
+    sm_l[wave][r] = lsum;
+  }
+  __syncthreads();
+
+  // merge the waves and write
+  for (int idx = threadIdx.x; idx < nh * D; idx += kWaves * 64) {
+    const int h = idx / D;
+    const int c = idx % D;
+    float M_ = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, sm_m[w][h]);
+    float o = 0.f, lse = -INFINITY;
+    if (M_ != -INFINITY) {
+      float ls = 0.f, os = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M_);  // 0 for an idle wave
+        ls = fmaf(sm_l[w][h], f, ls);
+        os = fmaf(sm_o[w][h][c], f, os);
+      }
+      o = os / ls;
+      lse = (M_ + __log2f(ls)) * kLn2;
+    }
+    const size_t row = static_cast<size_t>(s) * a.num_q_heads + h0 + h;
+    if (a.write_partials) {
+      a.o_part[(row * a.num_parts + part) * D + c] = o;
+      if (c == 0) a.lse_part[row * a.num_parts + part] = lse;
+    } else {
+      Tr::store(a.out, row * D + c, o);
+    }
+  }
+}
+
+template <class M, class Tr, int D>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int kWaves = 4;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int chunks = (group + 15) / 16;
+  dim3 grid(a.num_parts, a.num_kv_heads * chunks, a.num_seqs);
+  hipLaunchKernelGGL((decode_kernel<M, Tr, D, kWaves>), grid, dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <class M, class Tr>
+hipError_t launch_dim(const DecodeArgs& a, hipStream_t stream) {
+  return a.head_dim == 64 ? launch_t<M, Tr, 64>(a, stream) : launch_t<M, Tr, 128>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.dtype) {
+    case PA_F32: return launch_dim<MmaF32, F32>(a, stream);
+    case PA_F16: return launch_dim<MmaF16, F16>(a, stream);
+    default: return launch_dim<MmaBF16, BF16>(a, stream);
+  }
+}
+
+}  // namespace pa

@@ -34,7 +34,7 @@ struct DecodeArgs {
   void* out;
 };
 
-// Launch the decode kernel chosen for (dtype, head_dim, group size).
+// Launch the decode kernel chosen for (dtype, head_dim).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 struct ReduceArgs {
@@ -56,7 +56,8 @@ hipError_t launch_fill(void* dst, size_t bytes16, uint32_t pattern, hipStream_t 
 
 hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                           int32_t num_kv_heads, int32_t row_bytes, hipStream_t stream);
+                           int32_t num_kv_heads, int32_t row_bytes, int32_t elem_bytes,
+                           hipStream_t stream);
 
 hipError_t launch_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,

@@ -101,9 +101,9 @@ def _check(fn: str, status: int) -> None:
 
 
 def pool_desc(k_pool: torch.Tensor) -> PoolDesc:
-    """Descriptor of a [num_blocks][H_kv][16][d] pool tensor."""
-    nb, hkv, bs, d = k_pool.shape
-    return PoolDesc(nb, bs, hkv, d, TORCH_TO_PA.get(k_pool.dtype, -1))
+    """Descriptor of a K pool tensor shaped [num_blocks][H_kv][d / x][16][x]."""
+    nb, hkv, nchunk, bs, x = k_pool.shape
+    return PoolDesc(nb, bs, hkv, nchunk * x, TORCH_TO_PA.get(k_pool.dtype, -1))
 
 
 def pa_status_string(status: int) -> str:
@@ -164,7 +164,7 @@ def workspace_for(q, k_pool, max_context_len: int, partition_size: int):
     """A float32 workspace tensor for pa_decode's partials (None when unsplit)."""
     if partition_size <= 0:
         return None
-    n = pa_decode_workspace_bytes(q.shape[0], q.shape[1], k_pool.shape[3], max_context_len,
+    n = pa_decode_workspace_bytes(q.shape[0], q.shape[1], q.shape[2], max_context_len,
                                   partition_size)
     return torch.empty(n // 4, dtype=torch.float32, device=q.device)
 

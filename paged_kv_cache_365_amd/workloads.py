@@ -7,8 +7,13 @@ fp64 CPU oracle and the HIP library read the very same bytes from it.
 Layouts (they are the library's ABI, stated in ``include/pa.h``):
 
 * ``q``            ``[B][H_q][d]``            element dtype of the pool
-* ``k_pool/v_pool`` ``[num_blocks][H_kv][16][d]`` one (block, kv-head) tile of 16
-                    token rows is contiguous
+* ``k_pool``       ``[num_blocks][H_kv][d / x][16][x]``, x = 16 / element bytes:
+                    each token row is cut into 16-byte chunks and a tile stores
+                    chunk 0 of its 16 tokens, then chunk 1, ...
+* ``v_pool``       ``[num_blocks][H_kv][d][16]``: a tile stores column 0 of its
+                    16 tokens, then column 1, ...
+                    Either way one (block, kv-head) tile is 16 * d elements,
+                    contiguous.
 * ``block_tables`` ``int32 [B][max_blocks_per_seq]``; entry ``j`` of row ``s``
                     is the physical block holding tokens ``16j .. 16j+15`` of
                     sequence ``s``; entries past the live range are ``-1``
@@ -44,6 +49,18 @@ ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 # numpy storage type per element dtype (bf16 is carried as raw bits)
 STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 NAN_BITS = {"f32": np.uint32(0x7FC00000), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0)}
+
+
+def chunk_elems(dtype: str) -> int:
+    """Elements per 16-byte chunk of a K row."""
+    return 16 // ELEM_BYTES[dtype]
+
+
+def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
+    """(K pool shape, V pool shape) of the library's layout."""
+    x = chunk_elems(dtype)
+    return ((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x),
+            (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE))
 
 
 # --------------------------------------------------------------------------
@@ -107,8 +124,8 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     q: np.ndarray             # [B][H_q][d] storage dtype
-    k_pool: np.ndarray        # [NB][H_kv][16][d]
-    v_pool: np.ndarray        # [NB][H_kv][16][d]
+    k_pool: np.ndarray        # [NB][H_kv][d/x][16][x]
+    v_pool: np.ndarray        # [NB][H_kv][d][16]
     block_tables: np.ndarray  # int32 [B][max_blocks_per_seq]
     context_lens: np.ndarray  # int32 [B]
     scale: float              # float32 value carried as a Python float
@@ -219,34 +236,38 @@ def build_workload(
         cursor += n
     free = perm[used:]
 
-    shape = (pool_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
-    k_pool = normal(rng, shape, dtype)
-    v_pool = normal(rng, shape, dtype)
+    kshape, vshape = pool_shapes(pool_blocks, num_kv_heads, head_dim, dtype)
+    x = chunk_elems(dtype)
+    k_pool = normal(rng, kshape, dtype)
+    v_pool = normal(rng, vshape, dtype)
     if k_outlier_columns:
         # a few (kv-head, channel) columns of K carry x10 values: the per-channel
         # key outliers that motivate per-channel K quantisation on the pages
         cols = rng.choice(num_kv_heads * head_dim, size=k_outlier_columns, replace=False)
         for c in np.sort(cols):
             g, ch = divmod(int(c), head_dim)
-            k_pool[:, g, :, ch] = normal(rng, (pool_blocks, BLOCK_SIZE), dtype, gain=outlier_gain)
+            k_pool[:, g, ch // x, :, ch % x] = normal(rng, (pool_blocks, BLOCK_SIZE), dtype,
+                                                      gain=outlier_gain)
     q = normal(rng, (B, num_q_heads, head_dim), dtype)
 
     if poison:
         if len(free):
-            k_pool[free] = nan_fill((len(free),) + shape[1:], dtype)
-            v_pool[free] = nan_fill((len(free),) + shape[1:], dtype)
+            k_pool[free] = nan_fill((len(free),) + kshape[1:], dtype)
+            v_pool[free] = nan_fill((len(free),) + vshape[1:], dtype)
         for s in range(B):
             L = int(lens[s])
             o = L % BLOCK_SIZE
             if L == 0 or o == 0:
                 continue
             b = tables[s, L // BLOCK_SIZE]
+            kt = (num_kv_heads, head_dim // x, BLOCK_SIZE - o, x)
+            vt = (num_kv_heads, head_dim, BLOCK_SIZE - o)
             if tail_fill == "nan":
-                k_pool[b, :, o:, :] = nan_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype)
-                v_pool[b, :, o:, :] = nan_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype)
+                k_pool[b, :, :, o:, :] = nan_fill(kt, dtype)
+                v_pool[b, :, :, o:] = nan_fill(vt, dtype)
             elif tail_fill == "sentinel":
-                k_pool[b, :, o:, :] = const_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype, 1e3)
-                v_pool[b, :, o:, :] = const_fill((num_kv_heads, BLOCK_SIZE - o, head_dim), dtype, -1e3)
+                k_pool[b, :, :, o:, :] = const_fill(kt, dtype, 1e3)
+                v_pool[b, :, :, o:] = const_fill(vt, dtype, -1e3)
             else:
                 raise ValueError(tail_fill)
 

@@ -109,7 +109,8 @@ def test_slot_ids_bit_exact(i):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", wl.DTYPES)
 def test_init_pool(dtype):
-    kp = torch.full((5, 2, 16, 64), 3.0, dtype=TORCH_DTYPE[dtype], device=DEV)
+    ks, _ = wl.pool_shapes(5, 2, 64, dtype)
+    kp = torch.full(ks, 3.0, dtype=TORCH_DTYPE[dtype], device=DEV)
     vp = kp.clone()
     pa.pa_init_pool(kp, vp, 1)
     torch.cuda.synchronize()
@@ -123,8 +124,9 @@ def test_init_pool(dtype):
 def test_write_kv_bit_exact(dtype, d):
     rng = np.random.default_rng(5)
     nb, hkv, T = 12, 4, 37
-    kp = wl.normal(rng, (nb, hkv, 16, d), dtype)
-    vp = wl.normal(rng, (nb, hkv, 16, d), dtype)
+    ks, vs = wl.pool_shapes(nb, hkv, d, dtype)
+    kp = wl.normal(rng, ks, dtype)
+    vp = wl.normal(rng, vs, dtype)
     kn = wl.normal(rng, (T, hkv, d), dtype)
     vn = wl.normal(rng, (T, hkv, d), dtype)
     slots = rng.choice(nb * 16, size=T, replace=False).astype(np.int64)
@@ -264,7 +266,8 @@ def test_single_token_context_returns_v0_exactly(dtype):
     for s in range(3):
         b = w.block_tables[s, 0]
         for h in range(8):
-            assert np.array_equal(out[s, h].view(np.uint8), w.v_pool[b, h // 4, 0].view(np.uint8))
+            want = np.ascontiguousarray(w.v_pool[b, h // 4, :, 0])   # V tiles are [d][16]
+            assert np.array_equal(out[s, h].view(np.uint8), want.view(np.uint8))
 
 
 def test_uniform_v_and_poisoned_slots():
@@ -279,7 +282,7 @@ def test_uniform_v_and_poisoned_slots():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     # uniform V: every live V row of a (sequence, kv head) is the same vector
     c = wl.normal(np.random.default_rng(3), (2, 128), "bf16")
-    clean.v_pool[:] = c[None, :, None, :]
+    clean.v_pool[:] = c[None, :, :, None]                       # V tiles are [d][16]
     out = widen_f32(run_decode(upload(clean, DEV), 0)[0])
     want = oracle.widen(c, "bf16")
     for h in range(8):

@@ -28,7 +28,26 @@ BS = 16
 # ---------------------------------------------------------------------------
 # test-local helpers (independent of the oracle)
 # ---------------------------------------------------------------------------
-def scatter_to_pool(K, V, lens, rng, extra_blocks=3, dtype="f32"):
+def put_token(kp, vp, blk, off, k_row, v_row):
+    """Store one token's [H_kv][d] K and V rows at (blk, off) of pools in the
+    library layout, by this test's own index arithmetic: K elements go to
+    [chunk = c // x][off][c % x] with x = 16 bytes / element size, V elements
+    to [c][off]."""
+    x = 16 // kp.dtype.itemsize
+    Hkv, d = k_row.shape
+    for g in range(Hkv):
+        for c in range(d):
+            kp[blk, g, c // x, off, c % x] = k_row[g, c]
+            vp[blk, g, c, off] = v_row[g, c]
+
+
+def empty_pools(nb, Hkv, d, dtype, fill=0):
+    x = 16 // np.dtype(dtype).itemsize
+    return (np.full((nb, Hkv, d // x, BS, x), fill, dtype=dtype),
+            np.full((nb, Hkv, d, BS), fill, dtype=dtype))
+
+
+def scatter_to_pool(K, V, lens, rng, extra_blocks=3):
     """Contiguous K, V [B][Lmax][H_kv][d] -> a randomly permuted paged pool.
 
     Written here with its own index arithmetic so the paged oracle's gather is
@@ -40,17 +59,14 @@ def scatter_to_pool(K, V, lens, rng, extra_blocks=3, dtype="f32"):
     perm = rng.permutation(nb)
     width = max(max(need), 1)
     tables = np.full((B, width), -1, dtype=np.int32)
-    kp = np.zeros((nb, Hkv, BS, d), dtype=K.dtype)
-    vp = np.zeros((nb, Hkv, BS, d), dtype=V.dtype)
+    kp, vp = empty_pools(nb, Hkv, d, K.dtype)
     c = 0
     for s in range(B):
         for j in range(need[s]):
             tables[s, j] = perm[c]
             c += 1
         for t in range(int(lens[s])):
-            blk = tables[s, t // BS]
-            kp[blk, :, t % BS, :] = K[s, t]
-            vp[blk, :, t % BS, :] = V[s, t]
+            put_token(kp, vp, tables[s, t // BS], t % BS, K[s, t], V[s, t])
     return kp, vp, tables
 
 
@@ -187,17 +203,16 @@ def test_physical_permutation_invariance(seed):
 # T3 / T4 / T6 / T7 closed forms
 # ---------------------------------------------------------------------------
 def _one_seq_pool(K, V):
-    """One sequence, one KV head, tokens placed in blocks 2, 0, 3, 1, ..."""
+    """One sequence, one KV head, tokens placed in blocks 2, 0, 3, 1, ...; every
+    other slot is NaN."""
     L, d = K.shape
     nb = -(-L // BS) + 1
     order = [(2 * j + 2) % nb for j in range(nb - 1)]
     if len(set(order)) != len(order):
         order = list(range(nb - 1))
-    kp = np.full((nb, 1, BS, d), np.nan, dtype=K.dtype)
-    vp = np.full((nb, 1, BS, d), np.nan, dtype=V.dtype)
+    kp, vp = empty_pools(nb, 1, d, K.dtype, fill=np.nan)
     for t in range(L):
-        kp[order[t // BS], 0, t % BS] = K[t]
-        vp[order[t // BS], 0, t % BS] = V[t]
+        put_token(kp, vp, order[t // BS], t % BS, K[t][None], V[t][None])
     return kp, vp, np.array([order], dtype=np.int32)
 
 
@@ -343,8 +358,10 @@ def test_mqa_is_gqa_with_one_kv_head():
     to64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     for s in range(2):
         L = int(w.context_lens[s])
-        K = np.stack([to64(w.k_pool[w.block_tables[s, t // 16], :, t % 16, :]) for t in range(L)])
-        V = np.stack([to64(w.v_pool[w.block_tables[s, t // 16], :, t % 16, :]) for t in range(L)])
+        # read the tiles back by this test's own arithmetic: K [c // 8][o][c % 8], V [c][o]
+        K = np.stack([to64(np.array([w.k_pool[w.block_tables[s, t // 16], 0, c // 8, t % 16, c % 8]
+                                     for c in range(128)]))[None] for t in range(L)])
+        V = np.stack([to64(w.v_pool[w.block_tables[s, t // 16], 0, :, t % 16])[None] for t in range(L)])
         want = oracle.dense_attention(to64(w.q[s]), K, V, w.scale)
         np.testing.assert_allclose(got[s], want, rtol=0, atol=1e-12)
 
@@ -402,27 +419,27 @@ def test_poisoned_slots_are_never_read(tail):
 # ---------------------------------------------------------------------------
 # T13: KV append
 # ---------------------------------------------------------------------------
-def test_write_kv_places_rows_and_touches_nothing_else():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_write_kv_places_rows_and_touches_nothing_else(dtype):
     rng = np.random.default_rng(70)
     nb, Hkv, d, T = 6, 2, 64, 20
-    kp = wl.normal(rng, (nb, Hkv, BS, d), "bf16")
-    vp = wl.normal(rng, (nb, Hkv, BS, d), "bf16")
-    kn = wl.normal(rng, (T, Hkv, d), "bf16")
-    vn = wl.normal(rng, (T, Hkv, d), "bf16")
+    ks, vs = wl.pool_shapes(nb, Hkv, d, dtype)
+    kp = wl.normal(rng, ks, dtype)
+    vp = wl.normal(rng, vs, dtype)
+    kn = wl.normal(rng, (T, Hkv, d), dtype)
+    vn = wl.normal(rng, (T, Hkv, d), dtype)
     slots = rng.choice(nb * BS, size=T, replace=False).astype(np.int64)
     slots[[3, 11]] = -1
     k2, v2 = oracle.write_kv(kp, vp, kn, vn, slots)
-    owner = {int(s): i for i, s in enumerate(slots) if s >= 0}
-    for b in range(nb):
-        for o in range(BS):
-            i = owner.get(b * BS + o)
-            for g in range(Hkv):
-                if i is None:
-                    assert np.array_equal(k2[b, g, o], kp[b, g, o])
-                    assert np.array_equal(v2[b, g, o], vp[b, g, o])
-                else:
-                    assert np.array_equal(k2[b, g, o], kn[i, g])
-                    assert np.array_equal(v2[b, g, o], vn[i, g])
+    # expected pools built slot by slot with this test's own layout arithmetic
+    ke, ve = kp.copy(), vp.copy()
+    for i, sl in enumerate(slots):
+        if sl >= 0:
+            put_token(ke, ve, sl // BS, sl % BS, kn[i], vn[i])
+    assert np.array_equal(k2.view(np.uint8), ke.view(np.uint8))
+    assert np.array_equal(v2.view(np.uint8), ve.view(np.uint8))
+    changed = set(int(sl) for sl in slots if sl >= 0)
+    assert len(changed) == T - 2
     assert np.array_equal(kp, oracle.write_kv(kp, vp, kn, vn, np.full(T, -1))[0])
 
 
