@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kMaxReduceParts = 16384;  // partition weights staged in 64 KiB of LDS
+constexpr int kMaxReduceParts = 8192;  // partition weights staged in 32 KiB of LDS
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 

@@ -7,48 +7,98 @@ namespace pa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// pa_reduce: one workgroup per (sequence, query head), one thread per column.
-// The partition results are re-weighted by their share of the softmax mass:
-// with M = max lse_p, weight_p = exp(lse_p - M) / sum_q exp(lse_q - M).  This
-// is the same streaming-normaliser identity that makes the online softmax exact
-// (§4.2 of the ialgorithm.me page).  Partitions are visited in order.
+// pa_reduce: one workgroup of 256 threads per (sequence, query head).  The
+// partition results are re-weighted by their share of the softmax mass: with
+// M = max lse_p, weight_p = exp(lse_p - M) / sum_q exp(lse_q - M).  This is the
+// same streaming-normaliser identity that makes the online softmax exact (§4.2
+// of the ialgorithm.me page).
+//   1. weights: thread p < live partitions computes exp(lse_p - M) into LDS
+//      (M and the sum by a fixed-order block reduction);
+//   2. thread t owns 4 columns (t % (D/4)) and every G-th partition starting
+//      at t / (D/4), with G = 256 / (D/4) partition groups, float4 loads;
+//   3. the G group sums are added in group order through LDS.
+// Every sum has a fixed order, so the result is bit-reproducible.
 // ---------------------------------------------------------------------------
-template <class Tr>
-__global__ __launch_bounds__(128) void reduce_kernel(ReduceArgs a) {
-  extern __shared__ float sm_w[];  // [num_parts] weights
+constexpr int kReduceThreads = 256;
+
+__device__ __forceinline__ float block_max_256(float v, float* sm) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  __syncthreads();
+  return v;
+}
+
+template <class Tr, int D>
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
+  constexpr int kCols4 = D / 4;                       // float4 column groups
+  constexpr int kGroups = kReduceThreads / kCols4;    // partition groups
+  extern __shared__ float sm_w[];                     // [num_parts] weights
+  __shared__ float sm_red[4];
+  __shared__ float4 sm_acc[kGroups][kCols4];
+
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int c = threadIdx.x;
+  const int t = threadIdx.x;
   const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
   const int nv = (L + a.partition_tokens - 1) / a.partition_tokens;  // live partitions
-  const size_t r = static_cast<size_t>(s) * a.num_q_heads + h;
-  const float* lse = a.lse_part + r * a.num_parts;
+  const size_t row = static_cast<size_t>(s) * a.num_q_heads + h;
+  const float* lse = a.lse_part + row * a.num_parts;
 
-  float M = -INFINITY;
-  for (int p = 0; p < nv; ++p) M = fmaxf(M, lse[p]);
-  float o = 0.f;
-  if (M != -INFINITY) {
-    float sum = 0.f;
-    for (int p = threadIdx.x; p < nv; p += blockDim.x) sm_w[p] = __expf(lse[p] - M);
-    __syncthreads();
-    for (int p = 0; p < nv; ++p) sum += sm_w[p];
-    const float inv = 1.f / sum;
-    if (c < a.head_dim) {
-      const float* op = a.o_part + r * a.num_parts * a.head_dim + c;
-      float acc = 0.f;
-      for (int p = 0; p < nv; ++p) acc = fmaf(sm_w[p], op[static_cast<size_t>(p) * a.head_dim], acc);
-      o = acc * inv;
-    }
+  float mx = -INFINITY;
+  for (int p = t; p < nv; p += kReduceThreads) mx = fmaxf(mx, lse[p]);
+  const float M = block_max_256(mx, sm_red);
+  if (M == -INFINITY) {  // empty context: zero row (block-uniform branch)
+    for (int c = t; c < D; c += kReduceThreads) Tr::store(a.out, row * D + c, 0.f);
+    return;
   }
-  if (c < a.head_dim) Tr::store(a.out, r * a.head_dim + c, o);
+  for (int p = t; p < nv; p += kReduceThreads) sm_w[p] = __expf(lse[p] - M);
+  __syncthreads();
+
+  const int c4 = t % kCols4;
+  const int grp = t / kCols4;
+  const float4* op = reinterpret_cast<const float4*>(a.o_part + row * a.num_parts * D) + c4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = grp; p < nv; p += kGroups) {
+    const float w = sm_w[p];
+    const float4 v = op[static_cast<size_t>(p) * kCols4];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  sm_acc[grp][c4] = acc;
+  __syncthreads();
+  if (t < kCols4) {
+    float wsum = 0.f;
+    for (int p = 0; p < nv; ++p) wsum += sm_w[p];
+    const float inv = 1.f / wsum;
+    float4 o = sm_acc[0][t];
+#pragma unroll
+    for (int g = 1; g < kGroups; ++g) {
+      o.x += sm_acc[g][t].x;
+      o.y += sm_acc[g][t].y;
+      o.z += sm_acc[g][t].z;
+      o.w += sm_acc[g][t].w;
+    }
+    const size_t base = row * D + 4 * t;
+    Tr::store(a.out, base + 0, o.x * inv);
+    Tr::store(a.out, base + 1, o.y * inv);
+    Tr::store(a.out, base + 2, o.z * inv);
+    Tr::store(a.out, base + 3, o.w * inv);
+  }
 }
 
 template <class Tr>
 hipError_t launch_reduce_t(const ReduceArgs& a, hipStream_t stream) {
   dim3 grid(a.num_q_heads, a.num_seqs);
-  const int threads = a.head_dim <= 64 ? 64 : 128;
   const size_t lds = static_cast<size_t>(a.num_parts) * sizeof(float);
-  hipLaunchKernelGGL(reduce_kernel<Tr>, grid, dim3(threads), lds, stream, a);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL((reduce_kernel<Tr, 64>), grid, dim3(kReduceThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<Tr, 128>), grid, dim3(kReduceThreads), lds, stream, a);
   return hipGetLastError();
 }
 

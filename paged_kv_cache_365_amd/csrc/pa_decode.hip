@@ -57,6 +57,44 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kSlack = 8.0f;  // log2 headroom before the running maximum is raised
 
+// Load-ring depth and cache policy (compile-time; the defaults are the
+// measured best on MI355X).  Waves per workgroup are chosen per call.
+#ifndef PA_DECODE_DEPTH
+#define PA_DECODE_DEPTH 2  // 16-token blocks per wave in the load ring
+#endif
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1  // streaming (non-temporal) hint on 1: K and V, 2: K, 3: V loads
+#endif
+constexpr int kDepth = PA_DECODE_DEPTH;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <class T>
+struct NativeVec;
+template <>
+struct NativeVec<uint4> {
+  using type = u32x4;
+};
+template <>
+struct NativeVec<uint2> {
+  using type = u32x2;
+};
+
+// Load with or without the non-temporal hint.  K and V are each read once per
+// call (shared-prefix blocks aside), so the streaming policy keeps them from
+// displacing what the caches are better used for.
+template <bool kStream, class T>
+__device__ __forceinline__ T load16(const T* p) {
+  if constexpr (kStream) {
+    using N = typename NativeVec<T>::type;
+    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const N*>(p)));
+  } else {
+    return *p;
+  }
+}
+constexpr bool kStreamK = PA_DECODE_NT == 1 || PA_DECODE_NT == 2;
+constexpr bool kStreamV = PA_DECODE_NT == 1 || PA_DECODE_NT == 3;
+
 // ---------------------------------------------------------------------------
 // element-type specific operand handling
 // ---------------------------------------------------------------------------
@@ -220,15 +258,17 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const char* __restrict__ kbase = static_cast<const char*>(a.k_pool);
   const char* __restrict__ vbase = static_cast<const char*>(a.v_pool);
 
-  auto load = [&](int jb, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
-    const int phys = pa_physical_block(trow, jb, a.num_blocks);
+  // physical block of a (valid) logical block, read through the scalar cache
+  auto physical = [&](int jb) { return pa_physical_block(trow, jb, a.num_blocks); };
+
+  auto load = [&](int phys, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
     const size_t tile = pa_tile_offset(phys, g, a.num_kv_heads, D) * M::kBytes;
     const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
     const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + tile);
 #pragma unroll
-    for (int j = 0; j < kKLoads; ++j) kr[j] = kt[64 * j + lane];
+    for (int j = 0; j < kKLoads; ++j) kr[j] = load16<kStreamK>(kt + 64 * j + lane);
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = vt[(16 * cb + r) * 4 + qg];
+    for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = load16<kStreamV>(vt + (16 * cb + r) * 4 + qg);
   };
 
   auto consume = [&](int jb, const uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
@@ -265,21 +305,40 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     for (int cb = 0; cb < kColBlocks; ++cb) acc[cb] = M::pv(vr[cb], pop, acc[cb]);
   };
 
-  // two register sets: block jb is consumed while block jb + kWaves is loading
-  uint4 ka[kKLoads], kb[kKLoads];
-  VLoad va[kColBlocks], vb[kColBlocks];
-  int jb = blk_lo + wave;
-  if (jb < blk_hi) load(jb, ka, va);
-  while (jb < blk_hi) {
-    int jn = jb + kWaves;
-    if (jn < blk_hi) load(jn, kb, vb);
-    consume(jb, ka, va);
-    jb = jn;
-    if (jb >= blk_hi) break;
-    jn = jb + kWaves;
-    if (jn < blk_hi) load(jn, ka, va);
-    consume(jb, kb, vb);
-    jb = jn;
+  // A ring of kDepth register sets: the wave's i-th block (logical block
+  // blk_lo + wave + i * kWaves) is consumed while blocks i+1 .. i+kDepth-1 are
+  // in flight.  The physical id of the block to load next is read one
+  // iteration before its tile loads are issued.
+  uint4 kr[kDepth][kKLoads];
+  VLoad vr[kDepth][kColBlocks];
+  const int first = blk_lo + wave;
+  int next_phys = 0;
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d) {
+    const int jb = first + d * kWaves;
+    if (jb < blk_hi) load(physical(jb), kr[d], vr[d]);
+  }
+  {
+    const int jb = first + (kDepth - 1) * kWaves;
+    if (jb < blk_hi) next_phys = physical(jb);
+  }
+  for (int base = 0;; base += kDepth) {
+    bool done = false;
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int jb = first + (base + u) * kWaves;
+      if (jb >= blk_hi) {
+        done = true;
+        break;
+      }
+      const int jn = jb + (kDepth - 1) * kWaves;  // the block entering the ring
+      if (jn < blk_hi) {
+        load(next_phys, kr[(u + kDepth - 1) % kDepth], vr[(u + kDepth - 1) % kDepth]);
+        if (jn + kWaves < blk_hi) next_phys = physical(jn + kWaves);
+      }
+      consume(jb, kr[u], vr[u]);
+    }
+    if (done) break;
   }
 
   // this wave's results -> LDS
@@ -322,13 +381,19 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// Partitions of at least this many tokens get 8 wavefronts per workgroup, so
+// that each wave still streams a long run of blocks; shorter ones get 4.
+constexpr int kWideTokens = 2048;
+
 template <class M, class Tr, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int kWaves = 4;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int chunks = (group + 15) / 16;
   dim3 grid(a.num_parts, a.num_kv_heads * chunks, a.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<M, Tr, D, kWaves>), grid, dim3(kWaves * 64), 0, stream, a);
+  if (a.partition_tokens >= kWideTokens)
+    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8>), grid, dim3(8 * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4>), grid, dim3(4 * 64), 0, stream, a);
   return hipGetLastError();
 }
 

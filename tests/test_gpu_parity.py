@@ -18,7 +18,11 @@ from paged_kv_cache_365_amd.device import TORCH_DTYPE, to_numpy, to_torch, uploa
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
-LSE_TOL = 1e-4
+# A partition's log-sum-exp: the kernel sums the softmax weights after rounding
+# them to the KV element type (they are the P operand of the P.V matrix product),
+# so ln(sum) carries up to one unit roundoff of that type: 2^-8 for bfloat16,
+# 2^-11 for float16, none for float32; plus float32 noise.
+LSE_TOL = {"f32": 1e-4, "f16": 2.0 ** -11 + 1e-4, "bf16": 2.0 ** -8 + 1e-4}
 DEV = "cuda"
 
 
@@ -172,7 +176,7 @@ def test_decode_random_cases(case):
                                                 w.context_lens, w.scale, dtype, P)
         live = np.isfinite(wlse)
         assert np.array_equal(np.isfinite(lse_p), live), "empty partitions must be -inf"
-        assert np.abs(lse_p[live] - wlse[live]).max(initial=0) <= LSE_TOL
+        assert np.abs(lse_p[live] - wlse[live]).max(initial=0) <= LSE_TOL[dtype]
         assert_close(o_p[live], wo[live], TOL[dtype], "partials")
         assert not o_p[~live].any()
 
