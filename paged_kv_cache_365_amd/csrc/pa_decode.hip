@@ -381,9 +381,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   }
 }
 
-// Partitions of at least this many tokens get 8 wavefronts per workgroup, so
-// that each wave still streams a long run of blocks; shorter ones get 4.
-constexpr int kWideTokens = 2048;
+// Partitions of at least this many tokens get 8 wavefronts per workgroup (each
+// wave still streams a long run of blocks, and a ragged batch finishes more
+// evenly); shorter ones get 4.
+constexpr int kWideTokens = 4096;
 
 template <class M, class Tr, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
