@@ -11,7 +11,7 @@ from __future__ import annotations
 
 BLOCK_SIZE = 16
 MIN_UNITS = 512          # workgroups below which a context is split
-LONG_CONTEXT = 4096      # unsplit partitions this long stream well
+LONG_CONTEXT = 3072      # unsplit partitions this long stream well
 SPLIT_TOKENS = 1024      # smallest partition used when splitting
 
 

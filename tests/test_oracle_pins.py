@@ -458,3 +458,28 @@ def test_write_then_decode_matches_dense_append():
     got = oracle.paged_decode(q, kp, vp, tab, np.array([L + 1]), 0.125, "f32")[0]
     want = oracle.dense_attention(q[0].astype(np.float64), K.astype(np.float64), V.astype(np.float64), 0.125)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the dense brute force itself, against closed forms
+# ---------------------------------------------------------------------------
+def test_dense_closed_forms():
+    rng = np.random.default_rng(90)
+    L, Hkv, d = 7, 2, 64
+    K = rng.standard_normal((L, Hkv, d))
+    V = rng.standard_normal((L, Hkv, d))
+    q = rng.standard_normal((4, d))
+    # zero query: every key weighs 1/L, so each head returns the mean of its KV head's V
+    out = oracle.dense_attention(np.zeros((4, d)), K, V, 0.125)
+    for h in range(4):
+        np.testing.assert_allclose(out[h], V[:, h // 2].mean(axis=0), rtol=0, atol=1e-14)
+    # one token: the output is that token's V, whatever the query
+    out = oracle.dense_attention(q, K[:1], V[:1], 0.125)
+    for h in range(4):
+        np.testing.assert_allclose(out[h], V[0, h // 2], rtol=0, atol=1e-15)
+    # two tokens: logistic weights
+    x = [[0.125 * float(q[h] @ K[t, h // 2]) for t in range(2)] for h in range(4)]
+    out = oracle.dense_attention(q, K[:2], V[:2], 0.125)
+    for h in range(4):
+        w0 = 1.0 / (1.0 + math.exp(x[h][1] - x[h][0]))
+        np.testing.assert_allclose(out[h], w0 * V[0, h // 2] + (1 - w0) * V[1, h // 2], rtol=0, atol=1e-14)
