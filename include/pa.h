@@ -23,10 +23,18 @@
  *    value and nothing is launched; PA_ERR_HIP reports a failed launch.
  *  - Element dtype: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16), PA_BF16
  *    (bfloat16).  q, out, the pools and new K/V rows share the pool dtype.
- *  - KV pool layout: k_pool and v_pool are each [num_blocks][num_kv_heads][16][head_dim],
- *    dense, row-major.  One (physical block, kv head) tile of 16 token rows is
- *    contiguous (4 KiB for head_dim 128 in a 16-bit dtype).  Token slot
- *    = physical_block * 16 + offset.
+ *  - KV pool layout.  Both pools are arrays of tiles, one tile per (physical
+ *    block, kv head), block-major then head; a tile holds the 16 tokens of the
+ *    block, 16 * head_dim elements, contiguous (4 KiB for head_dim 128 in a
+ *    16-bit dtype).  Token slot = physical_block * 16 + offset.  Inside a tile:
+ *      k_pool  [num_blocks][num_kv_heads][head_dim / x][16][x], x = 16 bytes /
+ *              element size (8 for f16/bf16, 4 for f32): each token row is cut
+ *              into 16-byte chunks and the tile stores chunk 0 of its 16 tokens,
+ *              then chunk 1, ...;
+ *      v_pool  [num_blocks][num_kv_heads][head_dim][16]: the tile stores
+ *              element 0 of its 16 tokens, then element 1, ...
+ *    These orders make every operand of the decode kernel's matrix products a
+ *    contiguous per-lane load.
  *  - Block tables: int32 [num_seqs][max_blocks_per_seq], row-major.  Entry j of
  *    row s is the physical block of tokens 16j .. 16j+15 of sequence s.  Only
  *    the first ceil(context_lens[s] / 16) entries of a row are read.
@@ -78,7 +86,8 @@ pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int
 
 /* KV append: for each of num_tokens new tokens i, copy k_new[i] and v_new[i]
  * ([num_kv_heads][head_dim] each, pool dtype, so k_new is [num_tokens][H_kv][d])
- * bit for bit into slot slot_mapping[i] = physical * 16 + offset of both pools.
+ * bit for bit into slot slot_mapping[i] = physical * 16 + offset of both pools,
+ * in the tile layouts above.
  * A negative slot skips the token; slots >= num_blocks * 16 are also skipped.
  * Two tokens with the same slot race (the caller's contract).  This is the step
  * that puts the new token's K/V into the cache before attention, as the
