@@ -62,7 +62,8 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = -2, /* dtype, head_dim or block_size outside what is built */
   PA_ERR_MISALIGNED = -3,  /* a device pointer is not 16-byte aligned */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than pa_decode_workspace_bytes */
-  PA_ERR_HIP = -5          /* a kernel launch failed */
+  PA_ERR_HIP = -5,         /* a kernel launch failed */
+  PA_ERR_NO_SPACE = -6     /* block manager: the pool has too few free + cached blocks */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
@@ -148,6 +149,34 @@ pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_
                             const int32_t* context_lens, int32_t num_seqs,
                             int32_t max_context_len, int32_t num_blocks, int64_t* slot_ids,
                             hipStream_t stream);
+
+/* Copy whole blocks inside the pool: for each i < num_pairs, block
+ * src_dst[2i + 1] of both pools becomes a copy of block src_dst[2i] (every KV
+ * head, K and V).  This is the copy of a copy-on-write (§2.3 (2) of the
+ * blog.tanteng.space page: a sequence that writes into a block it shares gets
+ * its own copy first).  src_dst is int32 [num_pairs][2] in device
+ * memory.  A pair with an id outside [0, num_blocks) or with src == dst is
+ * skipped.  Destinations must be distinct and must not be sources of other
+ * pairs of the same call (they would race). */
+pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                         const int32_t* src_dst, int32_t num_pairs, hipStream_t stream);
+
+/* Swap support (preemption, §2.3 (1) of the blog.tanteng.space page: a full pool
+ * moves a request's blocks out to host memory and back later).
+ * pa_gather_blocks packs blocks block_ids[0 .. n) of both pools contiguously:
+ * block i goes to k_dst / v_dst at byte offset i * block_bytes, block_bytes =
+ * num_kv_heads * 16 * head_dim * element size (the pool's own tile order).
+ * pa_scatter_blocks is the inverse: k_src / v_src block i goes to pool block
+ * block_ids[i].  block_ids is int32 in device memory; ids outside the pool are
+ * skipped.  The packed buffers must be device-accessible (device memory, or
+ * pinned host memory) and 16-byte aligned; the caller moves them between host
+ * and device.  Scatter destinations must be distinct. */
+pa_status pa_gather_blocks(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
+                           const int32_t* block_ids, int32_t n, void* k_dst, void* v_dst,
+                           hipStream_t stream);
+pa_status pa_scatter_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                            const int32_t* block_ids, int32_t n, const void* k_src,
+                            const void* v_src, hipStream_t stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* pa_status_string(pa_status status);

@@ -253,3 +253,44 @@ def write_kv(k_pool, v_pool, k_new, v_new, slot_mapping):
                 k_out[b, g, c // x, o, c % x] = k_new[i, g, c]
                 v_out[b, g, c, o] = v_new[i, g, c]
     return k_out, v_out
+
+
+# --------------------------------------------------------------------------
+# whole-block moves  [P3 §2.3 (2): the copy of a copy-on-write;
+#                     P3 §2.3 (1): swapping a preempted request's blocks out]
+# --------------------------------------------------------------------------
+def copy_blocks(k_pool, v_pool, pairs):
+    """Copies of the pools in which block dst of each (src, dst) pair holds what
+    block src held before the call (every KV head, K and V).  Pairs naming a
+    block outside the pool, or with src == dst, are skipped."""
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    nb = k_pool.shape[0]
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if not (0 <= src < nb and 0 <= dst < nb) or src == dst:
+            continue
+        k_out[dst] = k_pool[src]
+        v_out[dst] = v_pool[src]
+    return k_out, v_out
+
+
+def gather_blocks(k_pool, v_pool, block_ids, k_dst, v_dst):
+    """Copies of the packed buffers (shaped [n] + one block's shape) in which
+    entry i holds pool block block_ids[i]; ids outside the pool leave entry i as
+    it was."""
+    k_out, v_out = k_dst.copy(), v_dst.copy()
+    for i, b in enumerate(np.asarray(block_ids, dtype=np.int64)):
+        if 0 <= b < k_pool.shape[0]:
+            k_out[i] = k_pool[b]
+            v_out[i] = v_pool[b]
+    return k_out, v_out
+
+
+def scatter_blocks(k_pool, v_pool, block_ids, k_src, v_src):
+    """Copies of the pools in which block block_ids[i] holds packed entry i; ids
+    outside the pool are skipped."""
+    k_out, v_out = k_pool.copy(), v_pool.copy()
+    for i, b in enumerate(np.asarray(block_ids, dtype=np.int64)):
+        if 0 <= b < k_pool.shape[0]:
+            k_out[b] = k_src[i]
+            v_out[b] = v_src[i]
+    return k_out, v_out

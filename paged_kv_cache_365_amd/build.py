@@ -1,7 +1,8 @@
 """Build ``libpa.so`` (the HIP library behind ``include/pa.h``) for gfx950.
 
-``python -m paged_kv_cache_365_amd.build`` compiles every ``csrc/*.hip`` with
-hipcc into ``paged_kv_cache_365_amd/libpa.so`` (in-tree, so the library travels
+``python -m paged_kv_cache_365_amd.build`` compiles every ``csrc/*.hip`` (device
+kernels and their C-ABI front end) and ``csrc/*.cpp`` (host-only code: the block
+manager) with hipcc into ``paged_kv_cache_365_amd/libpa.so`` (in-tree, so the library travels
 with the source tree).  Always recompiles.
 """
 from __future__ import annotations
@@ -37,7 +38,7 @@ def hipcc() -> str:
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:

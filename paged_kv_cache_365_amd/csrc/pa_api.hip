@@ -53,6 +53,7 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_MISALIGNED: return "PA_ERR_MISALIGNED";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_NO_SPACE: return "PA_ERR_NO_SPACE";
   }
   return "PA_ERR_UNKNOWN";
 }
@@ -186,6 +187,87 @@ pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t 
   a.dtype = out_dtype;
   a.out = out;
   return from_hip(pa::launch_reduce(a, stream));
+}
+
+pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                         const int32_t* src_dst, int32_t num_pairs, hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !src_dst) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(src_dst, 4)) return PA_ERR_MISALIGNED;
+  pa::BlockMoveArgs a{};
+  a.src_k = k_pool;
+  a.src_v = v_pool;
+  a.dst_k = k_pool;
+  a.dst_v = v_pool;
+  a.src_ids = src_dst;
+  a.src_stride = 2;
+  a.src_limit = pool->num_blocks;
+  a.dst_ids = src_dst + 1;
+  a.dst_stride = 2;
+  a.dst_limit = pool->num_blocks;
+  a.num_pairs = num_pairs;
+  a.block_bytes = pool_bytes(pool) / pool->num_blocks;
+  a.skip_equal = true;
+  return from_hip(pa::launch_block_move(a, stream));
+}
+
+pa_status pa_gather_blocks(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
+                           const int32_t* block_ids, int32_t n, void* k_dst, void* v_dst,
+                           hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_INVALID_ARG;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_ids || !k_dst || !v_dst) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_dst, 16) || !aligned(v_dst, 16) ||
+      !aligned(block_ids, 4))
+    return PA_ERR_MISALIGNED;
+  pa::BlockMoveArgs a{};
+  a.src_k = k_pool;
+  a.src_v = v_pool;
+  a.dst_k = k_dst;
+  a.dst_v = v_dst;
+  a.src_ids = block_ids;
+  a.src_stride = 1;
+  a.src_limit = pool->num_blocks;
+  a.dst_ids = nullptr;
+  a.dst_stride = 1;
+  a.dst_limit = n;
+  a.num_pairs = n;
+  a.block_bytes = pool_bytes(pool) / pool->num_blocks;
+  a.skip_equal = false;
+  return from_hip(pa::launch_block_move(a, stream));
+}
+
+pa_status pa_scatter_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
+                            const int32_t* block_ids, int32_t n, const void* k_src,
+                            const void* v_src, hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_INVALID_ARG;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !block_ids || !k_src || !v_src) return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_src, 16) || !aligned(v_src, 16) ||
+      !aligned(block_ids, 4))
+    return PA_ERR_MISALIGNED;
+  pa::BlockMoveArgs a{};
+  a.src_k = k_src;
+  a.src_v = v_src;
+  a.dst_k = k_pool;
+  a.dst_v = v_pool;
+  a.src_ids = nullptr;
+  a.src_stride = 1;
+  a.src_limit = n;
+  a.dst_ids = block_ids;
+  a.dst_stride = 1;
+  a.dst_limit = pool->num_blocks;
+  a.num_pairs = n;
+  a.block_bytes = pool_bytes(pool) / pool->num_blocks;
+  a.skip_equal = false;
+  return from_hip(pa::launch_block_move(a, stream));
 }
 
 pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -1,5 +1,6 @@
 // The small kernels around decode: the log-sum-exp merge of partition
-// partials, pool fill, KV append and the debug slot-id gather.
+// partials, pool fill, KV append, whole-block moves and the debug slot-id
+// gather.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -150,6 +151,37 @@ __global__ __launch_bounds__(256) void write_kv_kernel(char* k_pool, char* v_poo
 }
 
 // ---------------------------------------------------------------------------
+// whole-block moves (copy-on-write copies, swap gather / scatter).  Pair p
+// moves block src(p) of the source K and V buffers to block dst(p) of the
+// destination ones, where src(p) = src_ids[p * src_stride] (or p when src_ids
+// is null) and likewise for dst.  A block is block_bytes of contiguous tiles
+// (every KV head).  Pairs with an id outside its buffer's limit are skipped, and
+// so are src == dst pairs when skip_equal is set (a copy inside one pool).
+// blockIdx.z selects K (0) or V (1); pairs are strided over blockIdx.y.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void block_move_kernel(const uint4* src_k, const uint4* src_v,
+                                                         uint4* dst_k, uint4* dst_v,
+                                                         const int32_t* src_ids, int src_stride,
+                                                         int src_limit, const int32_t* dst_ids,
+                                                         int dst_stride, int dst_limit,
+                                                         int num_pairs, size_t block16,
+                                                         bool skip_equal) {
+  const uint4* src = blockIdx.z == 0 ? src_k : src_v;
+  uint4* dst = blockIdx.z == 0 ? dst_k : dst_v;
+  for (int p = blockIdx.y; p < num_pairs; p += gridDim.y) {
+    const int sb = src_ids ? src_ids[static_cast<size_t>(p) * src_stride] : p;
+    const int db = dst_ids ? dst_ids[static_cast<size_t>(p) * dst_stride] : p;
+    if (sb < 0 || sb >= src_limit || db < 0 || db >= dst_limit) continue;
+    if (skip_equal && sb == db) continue;
+    const uint4* s = src + static_cast<size_t>(sb) * block16;
+    uint4* d = dst + static_cast<size_t>(db) * block16;
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < block16;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+      d[i] = s[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // debug: the slots the decode kernels read, from the same device function
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void slot_ids_kernel(const int32_t* block_tables,
@@ -206,6 +238,19 @@ hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const 
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
                      slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * kBlockSize,
                      num_kv_heads, chunks_per_row);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream) {
+  const size_t block16 = a.block_bytes / 16;
+  const int64_t xg = static_cast<int64_t>((block16 + 255) / 256);
+  const unsigned gx = static_cast<unsigned>(xg < 1 ? 1 : (xg > 64 ? 64 : xg));
+  const unsigned gy = static_cast<unsigned>(a.num_pairs < 1 ? 1 : (a.num_pairs > 65535 ? 65535 : a.num_pairs));
+  hipLaunchKernelGGL(block_move_kernel, dim3(gx, gy, 2), dim3(256), 0, stream,
+                     static_cast<const uint4*>(a.src_k), static_cast<const uint4*>(a.src_v),
+                     static_cast<uint4*>(a.dst_k), static_cast<uint4*>(a.dst_v), a.src_ids,
+                     a.src_stride, a.src_limit, a.dst_ids, a.dst_stride, a.dst_limit, a.num_pairs,
+                     block16, a.skip_equal);
   return hipGetLastError();
 }
 

@@ -59,6 +59,23 @@ hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const 
                            int32_t num_kv_heads, int32_t row_bytes, int32_t elem_bytes,
                            hipStream_t stream);
 
+struct BlockMoveArgs {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int32_t* src_ids;  // null: pair index
+  int32_t src_stride;
+  int32_t src_limit;       // blocks in the source buffers
+  const int32_t* dst_ids;  // null: pair index
+  int32_t dst_stride;
+  int32_t dst_limit;
+  int32_t num_pairs;
+  size_t block_bytes;      // a multiple of 16
+  bool skip_equal;
+};
+hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream);
+
 hipError_t launch_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
                            int32_t num_blocks, int64_t* slot_ids, hipStream_t stream);

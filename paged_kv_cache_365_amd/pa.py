@@ -21,6 +21,7 @@ PA_ERR_UNSUPPORTED = -2
 PA_ERR_MISALIGNED = -3
 PA_ERR_WORKSPACE = -4
 PA_ERR_HIP = -5
+PA_ERR_NO_SPACE = -6
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
@@ -29,7 +30,8 @@ BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_init_pool", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
-           "pa_reduce", "pa_debug_slot_ids", "pa_status_string")
+           "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
+           "pa_scatter_blocks", "pa_status_string")
 
 
 class PAError(RuntimeError):
@@ -74,6 +76,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_reduce.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_debug_slot_ids.restype = ctypes.c_int
     lib.pa_debug_slot_ids.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [desc, vp, vp, vp, i32, vp]
+    lib.pa_gather_blocks.restype = ctypes.c_int
+    lib.pa_gather_blocks.argtypes = [desc, vp, vp, vp, i32, vp, vp, vp]
+    lib.pa_scatter_blocks.restype = ctypes.c_int
+    lib.pa_scatter_blocks.argtypes = [desc, vp, vp, vp, i32, vp, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -155,6 +163,28 @@ def pa_debug_slot_ids(block_tables, context_lens, max_context_len: int, num_bloc
     _check("pa_debug_slot_ids", load().pa_debug_slot_ids(
         _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
         int(max_context_len), int(num_blocks), _ptr(slot_ids), _stream(stream)))
+
+
+def pa_copy_blocks(k_pool, v_pool, src_dst, stream=None) -> None:
+    """src_dst: int32 device tensor [n][2] of (source, destination) blocks."""
+    desc = pool_desc(k_pool)
+    n = int(src_dst.shape[0]) if src_dst is not None else 0
+    _check("pa_copy_blocks", load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
+                                                   _ptr(src_dst), n, _stream(stream)))
+
+
+def pa_gather_blocks(k_pool, v_pool, block_ids, k_dst, v_dst, stream=None) -> None:
+    desc = pool_desc(k_pool)
+    _check("pa_gather_blocks", load().pa_gather_blocks(
+        ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
+        _ptr(k_dst), _ptr(v_dst), _stream(stream)))
+
+
+def pa_scatter_blocks(k_pool, v_pool, block_ids, k_src, v_src, stream=None) -> None:
+    desc = pool_desc(k_pool)
+    _check("pa_scatter_blocks", load().pa_scatter_blocks(
+        ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
+        _ptr(k_src), _ptr(v_src), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,254 @@
+"""GPU: whole-block moves bit for bit against the oracle, and a serving trace
+that runs the host block manager, the block-move kernels, KV append and decode
+together through the C ABI.
+
+The trace is the end-to-end check of the paged cache ([P3] = the page "LLM 推理
+优化：KV Cache、PagedAttention 与量化", §2.2-§2.3): sequences arrive with shared
+system prompts (prefix sharing), grow one token per decode step (on-demand
+blocks), fork (copy-on-write), finish (blocks return to the pool) and are
+swapped out and back in (preemption).  A token's K/V rows are a function of its
+whole token prefix -- as in a real model -- so shared and cached blocks are
+valid for every sequence that reaches them.  At checkpoints every live sequence
+is decoded on the GPU through the tables the manager produced and compared with
+the fp64 dense attention over the sequence's own token history.
+"""
+import random
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_365_amd import pa
+from paged_kv_cache_365_amd import workloads as wl
+from paged_kv_cache_365_amd.block_manager import BlockManager
+from paged_kv_cache_365_amd.device import TORCH_DTYPE, to_numpy, to_torch, widen_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pa.load()
+
+
+def _bytes(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# block moves: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d,hkv", [("bf16", 128, 8), ("f32", 64, 2), ("f16", 128, 1)])
+def test_copy_blocks_bit_exact(dtype, d, hkv):
+    rng = np.random.default_rng(11)
+    nb = 40
+    ks, vs = wl.pool_shapes(nb, hkv, d, dtype)
+    kp, vp = wl.normal(rng, ks, dtype), wl.normal(rng, vs, dtype)
+    pairs = np.array([[3, 30], [7, 7], [12, 31], [-1, 5], [2, nb], [39, 0], [4, 32]], np.int32)
+    want_k, want_v = oracle.copy_blocks(kp, vp, pairs)
+    tk, tv = to_torch(kp, dtype, DEV), to_torch(vp, dtype, DEV)
+    pa.pa_copy_blocks(tk, tv, torch.from_numpy(pairs).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bytes(to_numpy(tk)), _bytes(want_k))
+    assert np.array_equal(_bytes(to_numpy(tv)), _bytes(want_v))
+
+
+@pytest.mark.parametrize("dtype,d,hkv", [("bf16", 128, 8), ("f32", 64, 4)])
+def test_gather_scatter_bit_exact(dtype, d, hkv):
+    rng = np.random.default_rng(12)
+    nb = 33
+    ks, vs = wl.pool_shapes(nb, hkv, d, dtype)
+    kp, vp = wl.normal(rng, ks, dtype), wl.normal(rng, vs, dtype)
+    ids = np.array([5, 0, 32, -2, 17, 40, 9], np.int32)
+    kz = np.zeros((len(ids),) + ks[1:], kp.dtype)
+    vz = np.zeros((len(ids),) + vs[1:], vp.dtype)
+    want_k, want_v = oracle.gather_blocks(kp, vp, ids, kz, vz)
+    tk, tv = to_torch(kp, dtype, DEV), to_torch(vp, dtype, DEV)
+    gk, gv = to_torch(kz, dtype, DEV), to_torch(vz, dtype, DEV)
+    tids = torch.from_numpy(ids).to(DEV)
+    pa.pa_gather_blocks(tk, tv, tids, gk, gv)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bytes(to_numpy(gk)), _bytes(want_k))
+    assert np.array_equal(_bytes(to_numpy(gv)), _bytes(want_v))
+    # scatter the packed blocks to other ids of a zeroed pool
+    dst = np.array([1, 2, 3, 4, -1, 6, 30], np.int32)
+    want_k2, want_v2 = oracle.scatter_blocks(np.zeros_like(kp), np.zeros_like(vp), dst, want_k, want_v)
+    zk, zv = torch.zeros_like(tk), torch.zeros_like(tv)
+    pa.pa_scatter_blocks(zk, zv, torch.from_numpy(dst).to(DEV), gk, gv)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bytes(to_numpy(zk)), _bytes(want_k2))
+    assert np.array_equal(_bytes(to_numpy(zv)), _bytes(want_v2))
+
+
+# ---------------------------------------------------------------------------
+# the serving trace
+# ---------------------------------------------------------------------------
+class Serving:
+    def __init__(self, seed, num_blocks, hkv, hq, d, dtype):
+        self.rnd = random.Random(seed)
+        self.nb, self.hkv, self.hq, self.d, self.dtype = num_blocks, hkv, hq, d, dtype
+        self.bm = BlockManager(num_blocks)
+        ks, vs = wl.pool_shapes(num_blocks, hkv, d, dtype)
+        self.kp = torch.empty(ks, dtype=TORCH_DTYPE[dtype], device=DEV)
+        self.vp = torch.empty(vs, dtype=TORCH_DTYPE[dtype], device=DEV)
+        pa.pa_init_pool(self.kp, self.vp, 1)     # NaN: a slot never written must never be read
+        self.tokens = {}     # seq -> token history
+        self.chain = {}      # seq -> running CRC of its prefix, per position
+        self.saved = {}      # swapped-out seq -> (packed K, packed V) on the host
+        self.next_id = 0
+        self.scale = float(np.float32(1.0 / np.sqrt(d)))
+        self.checks = 0
+
+    # K/V of a token: a function of its whole prefix (content-addressed)
+    def rows(self, crcs):
+        k = np.empty((len(crcs), self.hkv, self.d), wl.STORAGE[self.dtype])
+        v = np.empty_like(k)
+        for i, c in enumerate(crcs):
+            r = np.random.default_rng(c)
+            k[i] = wl.normal(r, (self.hkv, self.d), self.dtype)
+            v[i] = wl.normal(r, (self.hkv, self.d), self.dtype)
+        return k, v
+
+    def extend(self, seq, toks):
+        h = self.tokens.setdefault(seq, [])
+        c = self.chain.setdefault(seq, [])
+        for t in toks:
+            prev = c[-1] if c else 0
+            h.append(t)
+            c.append(zlib.crc32(np.int32(t).tobytes(), prev))
+
+    def write(self, seq_slots):
+        """seq_slots: list of (seq, position, slot)."""
+        if not seq_slots:
+            return
+        crcs = [self.chain[s][t] for s, t, _ in seq_slots]
+        k, v = self.rows(crcs)
+        slots = torch.tensor([sl for _, _, sl in seq_slots], dtype=torch.int64, device=DEV)
+        pa.pa_write_kv(self.kp, self.vp, to_torch(k, self.dtype, DEV), to_torch(v, self.dtype, DEV),
+                       slots)
+
+    def copy(self, pairs):
+        if len(pairs):
+            pa.pa_copy_blocks(self.kp, self.vp,
+                              torch.tensor(np.asarray(pairs, np.int32).reshape(-1, 2), device=DEV))
+
+    def add(self, prompt):
+        seq = self.next_id
+        self.next_id += 1
+        self.bm.add_seq(seq)
+        cached = self.bm.match_prefix(seq, prompt)
+        try:
+            slots, cp = self.bm.append(seq, len(prompt) - cached, prompt[cached:])
+        except pa.PAError as e:
+            assert e.status == pa.PA_ERR_NO_SPACE
+            self.bm.free_seq(seq)
+            return None
+        assert cp is None
+        self.extend(seq, prompt)
+        self.write([(seq, cached + i, int(sl)) for i, sl in enumerate(slots)])
+        return seq
+
+    def step(self, seqs):
+        toks = [self.rnd.randrange(4) for _ in seqs]
+        try:
+            slots, copies = self.bm.append_step(seqs, toks)
+        except pa.PAError as e:
+            assert e.status == pa.PA_ERR_NO_SPACE
+            return False
+        self.copy(copies)                       # copy-on-write before the writes
+        for s, t in zip(seqs, toks):
+            self.extend(s, [t])
+        self.write([(s, len(self.tokens[s]) - 1, int(sl)) for s, sl in zip(seqs, slots)])
+        return True
+
+    def fork(self, parent):
+        child = self.next_id
+        self.next_id += 1
+        self.bm.fork(parent, child)
+        self.tokens[child] = list(self.tokens[parent])
+        self.chain[child] = list(self.chain[parent])
+        return child
+
+    def swap_out(self, seq):
+        table, L = self.bm.swap_out(seq)
+        ids = torch.from_numpy(table).to(DEV)
+        n = len(table)
+        gk = torch.empty((n,) + tuple(self.kp.shape[1:]), dtype=self.kp.dtype, device=DEV)
+        gv = torch.empty((n,) + tuple(self.vp.shape[1:]), dtype=self.vp.dtype, device=DEV)
+        pa.pa_gather_blocks(self.kp, self.vp, ids, gk, gv)   # before anything reuses the blocks
+        self.saved[seq] = (gk.cpu(), gv.cpu())
+
+    def swap_in(self, seq):
+        try:
+            table = self.bm.swap_in(seq)
+        except pa.PAError as e:
+            assert e.status == pa.PA_ERR_NO_SPACE
+            return False
+        gk, gv = self.saved.pop(seq)
+        pa.pa_scatter_blocks(self.kp, self.vp, torch.from_numpy(table).to(DEV), gk.to(DEV),
+                             gv.to(DEV))
+        return True
+
+    def check(self, live, partition):
+        if not live:
+            return
+        tables = [self.bm.table(s) for s in live]
+        width = max(max(len(t) for t, _ in tables), 1)
+        tab, lens = self.bm.fill_tables(live, width)
+        maxlen = int(lens.max())
+        rng = np.random.default_rng(self.checks)
+        self.checks += 1
+        q = wl.normal(rng, (len(live), self.hq, self.d), self.dtype)
+        out = pa.paged_attention(to_torch(q, self.dtype, DEV), self.kp, self.vp,
+                                 torch.from_numpy(tab).to(DEV), torch.from_numpy(lens).to(DEV),
+                                 maxlen, self.scale, partition_size=partition)
+        torch.cuda.synchronize()
+        got = widen_f32(out)
+        for i, s in enumerate(live):
+            assert lens[i] == len(self.tokens[s])
+            k, v = self.rows(self.chain[s])
+            want = oracle.dense_attention(oracle.widen(q[i], self.dtype), oracle.widen(k, self.dtype),
+                                          oracle.widen(v, self.dtype), self.scale)
+            err = np.abs(got[i] - want).max()
+            assert np.isfinite(got[i]).all() and err <= TOL[self.dtype], (s, err)
+
+
+@pytest.mark.parametrize("seed,dtype,hkv,hq,d", [(0, "bf16", 2, 16, 128), (1, "f32", 2, 4, 64),
+                                                 (2, "f16", 1, 8, 128)])
+def test_serving_trace(seed, dtype, hkv, hq, d):
+    srv = Serving(seed, num_blocks=80, hkv=hkv, hq=hq, d=d, dtype=dtype)
+    rnd = random.Random(1000 + seed)
+    sys_prompts = [[rnd.randrange(4) for _ in range(n)] for n in (32, 48, 70)]
+    live, swapped = [], []
+    for op in range(160):
+        r = rnd.random()
+        if r < 0.2 or not live:
+            prompt = rnd.choice(sys_prompts) + [rnd.randrange(4) for _ in range(rnd.randrange(1, 30))]
+            s = srv.add(prompt)
+            if s is not None:
+                live.append(s)
+        elif r < 0.65:
+            srv.step(rnd.sample(live, rnd.randint(1, len(live))))
+        elif r < 0.72:
+            live.append(srv.fork(rnd.choice(live)))
+        elif r < 0.82:
+            srv.bm.free_seq(live.pop(rnd.randrange(len(live))))
+        elif r < 0.9:
+            s = live.pop(rnd.randrange(len(live)))
+            srv.swap_out(s)
+            swapped.append(s)
+        elif swapped:
+            if srv.swap_in(swapped[0]):
+                live.append(swapped.pop(0))
+        if op % 40 == 39:
+            srv.check(live, partition=0)
+            srv.check(live, partition=32)
+    srv.check(live, partition=0)
+    st = srv.bm.stats()
+    assert st["prefix_hit_blocks"] > 0 and st["cow_copies"] > 0
+    assert srv.checks >= 9

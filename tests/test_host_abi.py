@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     for code, name in [(0, "PA_OK"), (-1, "PA_ERR_INVALID_ARG"), (-2, "PA_ERR_UNSUPPORTED"),
-                       (-3, "PA_ERR_MISALIGNED"), (-4, "PA_ERR_WORKSPACE"), (-5, "PA_ERR_HIP")]:
+                       (-3, "PA_ERR_MISALIGNED"), (-4, "PA_ERR_WORKSPACE"), (-5, "PA_ERR_HIP"),
+                       (-6, "PA_ERR_NO_SPACE")]:
         assert pa.pa_status_string(code) == name
     assert pa.pa_status_string(7) == "PA_ERR_UNKNOWN"
 
@@ -116,3 +117,18 @@ def test_binding_raises_on_error_status(lib):
     with pytest.raises(pa.PAError) as e:
         pa._check("pa_decode", pa.PA_ERR_WORKSPACE)
     assert "PA_ERR_WORKSPACE" in str(e.value)
+
+
+def test_block_moves_reject_bad_arguments(lib):
+    d = _desc()
+    c, g, s = lib.pa_copy_blocks, lib.pa_gather_blocks, lib.pa_scatter_blocks
+    assert c(ctypes.byref(d), FAKE, FAKE, FAKE, 0, None) == pa.PA_OK         # nothing to do
+    assert c(ctypes.byref(d), FAKE, FAKE, FAKE, -1, None) == pa.PA_ERR_INVALID_ARG
+    assert c(ctypes.byref(d), FAKE, FAKE, None, 2, None) == pa.PA_ERR_INVALID_ARG
+    assert c(ctypes.byref(d), FAKE + 8, FAKE, FAKE, 2, None) == pa.PA_ERR_MISALIGNED
+    assert c(ctypes.byref(_desc(bs=8)), FAKE, FAKE, FAKE, 2, None) == pa.PA_ERR_UNSUPPORTED
+    assert g(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == pa.PA_OK
+    assert g(ctypes.byref(d), FAKE, FAKE, FAKE, 2, None, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert g(ctypes.byref(d), FAKE, FAKE, FAKE, 2, FAKE + 4, FAKE, None) == pa.PA_ERR_MISALIGNED
+    assert s(ctypes.byref(d), FAKE, FAKE, FAKE, -3, FAKE, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert s(ctypes.byref(d), FAKE, FAKE, FAKE + 2, 2, FAKE, FAKE, None) == pa.PA_ERR_MISALIGNED

@@ -2,7 +2,9 @@
 
 Every case copies the oracle, the generators and the pins into a scratch
 directory, plants one mistake in the copied oracle (on the CPU, never in the
-library), and runs the pins there; the run must fail.
+library), and runs the pins there; the run must fail.  The block-manager model
+is mutated the same way and checked by the model-only tests of
+tests/test_block_manager.py (the library is not copied).
 """
 import os
 import shutil
@@ -56,4 +58,43 @@ def test_planted_mistake_is_caught(name, source, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_pins.py"], cwd=tmp_path, capture_output=True, text=True,
                        timeout=300)
+    assert r.returncode != 0, f"no pin caught the planted mistake {name}:\n{r.stdout[-2000:]}"
+
+
+BM_MODEL = os.path.join(ROOT, "oracle", "block_manager.py")
+BM_MUTATIONS = {
+    "cow_never": [("elif i == 0 and self.ref[table[-1]] > 1:", "elif False:")],
+    "cow_no_decref": [("                self.ref[src] -= 1              # still referenced by another table\n", "")],
+    "release_forward": [("for b in reversed(self.tables.pop(seq)):", "for b in self.tables.pop(seq):")],
+    "evict_newest": [("self.cached.popitem(last=False)", "self.cached.popitem(last=True)")],
+    "match_whole_prompt": [("n_blocks = max(len(prompt) - 1, 0) // BLOCK_SIZE",
+                            "n_blocks = len(prompt) // BLOCK_SIZE")],
+    "key_without_prefix": [("key = tuple(prompt[: (i + 1) * BLOCK_SIZE])",
+                            "key = tuple(prompt[i * BLOCK_SIZE:(i + 1) * BLOCK_SIZE])"),
+                           ("                    key = tuple(toks)\n",
+                            "                    key = tuple(toks[-BLOCK_SIZE:])\n")],
+    "cached_to_stack": [("            if b in self.key_of:\n                self.cached[b] = True",
+                         "            if False:\n                self.cached[b] = True")],
+    "stack_fifo": [("return self.free.pop()", "return self.free.pop(0)")],
+    "fork_no_incref": [("        for b in self.tables[child]:\n            self.ref[b] += 1\n", "")],
+    "needed_without_cow": [("        return new + cow\n", "        return new\n")],
+    "swap_in_shares": [("            b = self._take()\n            self.ref[b] = 1\n            table.append(b)\n        self.tables[seq] = table",
+                        "            b = self._take()\n            self.ref[b] = 1\n            table.append(0)\n        self.tables[seq] = table")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(BM_MUTATIONS))
+def test_planted_block_manager_mistake_is_caught(name, tmp_path):
+    source = open(BM_MODEL).read()
+    for old, new in BM_MUTATIONS[name]:
+        assert source.count(old) == 1, f"mutation {name} no longer matches the model source"
+        source = source.replace(old, new)
+    for sub in ("oracle", "tests", "paged_kv_cache_365_amd"):
+        shutil.copytree(os.path.join(ROOT, sub), tmp_path / sub,
+                        ignore=shutil.ignore_patterns("__pycache__", "*.so", "csrc"))
+    (tmp_path / "oracle" / "block_manager.py").write_text(source)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "-k", "not lib and not exports", "tests/test_block_manager.py"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert "passed" in r.stdout or "failed" in r.stdout, r.stdout[-2000:]
     assert r.returncode != 0, f"no pin caught the planted mistake {name}:\n{r.stdout[-2000:]}"

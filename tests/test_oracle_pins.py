@@ -461,6 +461,69 @@ def test_write_then_decode_matches_dense_append():
 
 
 # ---------------------------------------------------------------------------
+# whole-block moves (copy-on-write copy, swap gather / scatter) [P3 §2.3]
+# ---------------------------------------------------------------------------
+def _random_paged(rng, nb, Hkv, d, dtype):
+    ks, vs = wl.pool_shapes(nb, Hkv, d, dtype)
+    return wl.normal(rng, ks, dtype), wl.normal(rng, vs, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_copy_blocks_reads_through_the_copy(dtype):
+    """After a copy, attention through a table naming the destination equals
+    attention through the source before the copy; blocks that are no destination
+    keep every bit; skipped pairs change nothing."""
+    rng = np.random.default_rng(72)
+    nb, Hkv, Hq, d = 10, 2, 4, 64
+    kp, vp = _random_paged(rng, nb, Hkv, d, dtype)
+    q = wl.normal(rng, (1, Hq, d), dtype)
+    pairs = [(3, 7), (5, 5), (1, 12), (-1, 2), (4, 8)]
+    k2, v2 = oracle.copy_blocks(kp, vp, pairs)
+    for src, dst in [(3, 7), (4, 8)]:
+        before = oracle.paged_decode(q, kp, vp, np.array([[src]], np.int32), np.array([13]), 0.125, dtype)
+        after = oracle.paged_decode(q, k2, v2, np.array([[dst]], np.int32), np.array([13]), 0.125, dtype)
+        assert np.array_equal(before, after)
+    for b in range(nb):
+        if b not in (7, 8):
+            assert np.array_equal(k2[b].view(np.uint8), kp[b].view(np.uint8))
+            assert np.array_equal(v2[b].view(np.uint8), vp[b].view(np.uint8))
+    # a later write into the copy leaves the source's readers untouched (copy-on-write)
+    kn = wl.normal(rng, (1, Hkv, d), dtype)
+    k3, v3 = oracle.write_kv(k2, v2, kn, kn, np.array([7 * BS + 2]))
+    src_view = oracle.paged_decode(q, k3, v3, np.array([[3]], np.int32), np.array([13]), 0.125, dtype)
+    assert np.array_equal(src_view, oracle.paged_decode(q, kp, vp, np.array([[3]], np.int32),
+                                                        np.array([13]), 0.125, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_gather_scatter_round_trip_is_a_relabelling(dtype):
+    """Swap out (gather) then in (scatter into other blocks) and rewrite the table:
+    the decode output is bit-identical, as for any relabelling of physical ids."""
+    rng = np.random.default_rng(73)
+    nb, Hkv, Hq, d = 12, 2, 4, 128
+    kp, vp = _random_paged(rng, nb, Hkv, d, dtype)
+    q = wl.normal(rng, (1, Hq, d), dtype)
+    table = np.array([[4, 9, 2]], np.int32)
+    ref = oracle.paged_decode(q, kp, vp, table, np.array([40]), 0.1, dtype)
+    ids = table[0]
+    kz = np.zeros((3,) + kp.shape[1:], kp.dtype)
+    vz = np.zeros((3,) + vp.shape[1:], vp.dtype)
+    kb, vb = oracle.gather_blocks(kp, vp, ids, kz, vz)
+    new_ids = np.array([11, 0, 5], np.int32)
+    wiped = np.full_like(kp, 0), np.full_like(vp, 0)
+    k2, v2 = oracle.scatter_blocks(wiped[0], wiped[1], new_ids, kb, vb)
+    got = oracle.paged_decode(q, k2, v2, new_ids[None], np.array([40]), 0.1, dtype)
+    assert np.array_equal(got, ref)
+    # gathering back to the same ids restores the pool exactly; bad ids are skipped
+    k3, v3 = oracle.scatter_blocks(kp * 0, vp * 0, np.array([4, 9, 2, -3, 99]),
+                                   np.concatenate([kb, kb[:2]]), np.concatenate([vb, vb[:2]]))
+    for b in (4, 9, 2):
+        assert np.array_equal(k3[b].view(np.uint8), kp[b].view(np.uint8))
+    kg, _ = oracle.gather_blocks(kp, vp, np.array([-1, 3]), kz[:2] + 0, vz[:2] + 0)
+    assert not kg[0].any() and np.array_equal(kg[1].view(np.uint8), kp[3].view(np.uint8))
+
+
+# ---------------------------------------------------------------------------
 # the dense brute force itself, against closed forms
 # ---------------------------------------------------------------------------
 def test_dense_closed_forms():
