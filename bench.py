@@ -59,22 +59,24 @@ def stored_traffic(workload: str, partition: int):
     return entry.get("hbm_bytes_per_launch")
 
 
-def decode_kernel_bytes(w, partition: int) -> int:
-    """Algorithmic bytes one pa_decode launch must move: K and V rows of every live
-    token (2 * H_kv * d * element bytes per token), q, live block-table entries and
-    context lengths, plus the output rows when it writes them itself (unsplit).
-    Split-context partials are not algorithmic and are not counted."""
+def decode_kernel_bytes(w, partition: int, query_tokens: int = 1) -> int:
+    """Algorithmic bytes one pa_decode (or pa_verify_decode) launch must move: K and
+    V rows of every live token (2 * H_kv * d * element bytes per token), q, live
+    block-table entries and context lengths, plus the output rows when it writes
+    them itself (unsplit).  Split-context partials are not algorithmic and are not
+    counted."""
     from paged_kv_cache_365_amd.workloads import ELEM_BYTES
     e = ELEM_BYTES[w.dtype]
     live = int(((w.context_lens.astype("int64") + 15) // 16).sum())
-    qo = w.num_seqs * w.num_q_heads * w.head_dim * e
+    qo = query_tokens * w.num_seqs * w.num_q_heads * w.head_dim * e
     return w.kv_bytes_logical() + qo * (1 if partition else 2) + 4 * live + 4 * w.num_seqs
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0):
+def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0, verify_q=None):
     """The fp64 oracle, single-threaded, on the same workload: whole passes over
     every sequence until about ``min_seconds`` have elapsed (bounded by
-    ``max_seconds``; the last pass may stop early)."""
+    ``max_seconds``; the last pass may stop early).  ``verify_q`` [B][T][H_q][d]:
+    time the verify oracle over that draft instead."""
     import oracle
     from threadpoolctl import threadpool_limits
     B = w.num_seqs
@@ -83,19 +85,25 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0):
         done_seqs = 0
         while time.perf_counter() - t0 < min_seconds:
             for s in range(B):
-                oracle.paged_decode(w.q[s:s + 1], w.k_pool, w.v_pool, w.block_tables[s:s + 1],
-                                    w.context_lens[s:s + 1], w.scale, w.dtype)
+                if verify_q is None:
+                    oracle.paged_decode(w.q[s:s + 1], w.k_pool, w.v_pool, w.block_tables[s:s + 1],
+                                        w.context_lens[s:s + 1], w.scale, w.dtype)
+                else:
+                    oracle.paged_verify(verify_q[s:s + 1], w.k_pool, w.v_pool,
+                                        w.block_tables[s:s + 1], w.context_lens[s:s + 1],
+                                        w.scale, w.dtype)
                 done_seqs += 1
                 if time.perf_counter() - t0 > max_seconds:
                     break
         dt = time.perf_counter() - t0
     frac = done_seqs / B
-    gbps = w.algorithmic_bytes() * frac / dt / 1e9
+    T = 1 if verify_q is None else verify_q.shape[1]
+    gbps = w.algorithmic_bytes(query_tokens=T) * frac / dt / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done_seqs} sequences ({frac:.2f} passes over all {B} sequences x "
                       f"{w.num_q_heads} heads of the workload), numpy float64, one thread, "
                       f"{dt:.1f} s",
-            "tokens_per_s": round(done_seqs / dt, 3)}
+            "tokens_per_s": round(done_seqs * T / dt, 3)}
 
 
 def copy_bandwidth(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
@@ -123,6 +131,9 @@ def main() -> int:
     ap.add_argument("--tuned", action="store_true",
                     help="use the tuned partition size even where the workload names its own")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--verify", type=int, default=0, metavar="T",
+                    help="time the speculative-decoding verify call over a T-token draft "
+                         "(pa_verify_decode) instead of single-token decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for counter calibration)")
@@ -150,9 +161,20 @@ def main() -> int:
     w = wl.make_config(args.config, args.seed)
     P = tuning.partition_for(w, own=not args.tuned) if args.partition is None else args.partition
     d = upload(w, "cuda")
-    out = torch.empty_like(d.q)
-    ws = pa.workspace_for(d.q, d.k_pool, d.max_context_len, P)
+    T = max(args.verify, 1)
     B, Hq, D = d.q.shape
+    if args.verify:
+        from paged_kv_cache_365_amd.device import to_torch
+        q_np = wl.normal(np.random.default_rng(7), (B, T, Hq, D), w.dtype)
+        qv = to_torch(q_np, w.dtype, "cuda")
+        out = torch.empty_like(qv)
+        ws = None
+        if P:
+            n = pa.pa_decode_workspace_bytes(B, T * Hq, D, d.max_context_len, P)
+            ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    else:
+        out = torch.empty_like(d.q)
+        ws = pa.workspace_for(d.q, d.k_pool, d.max_context_len, P)
     stream = torch.cuda.current_stream()
     log(f"{w.name}: B={B} Hq={Hq} Hkv={w.num_kv_heads} d={D} dtype={w.dtype} "
         f"maxlen={w.max_context_len} partition={P}")
@@ -167,19 +189,18 @@ def main() -> int:
         after reduce)."""
         if ev is not None:
             ev[0].record(stream)
-        if P:
-            pa.pa_decode(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
-                         d.max_context_len, d.scale, P, ws, None, stream)
-            if ev is not None:
-                ev[1].record(stream)
-            pa.pa_reduce(ws, d.context_lens, B, Hq, D, d.max_context_len, P, out, stream)
-            if ev is not None:
-                ev[2].record(stream)
+        if args.verify:
+            pa.pa_verify_decode(qv, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                                d.max_context_len, d.scale, P, ws, None if P else out, stream)
         else:
             pa.pa_decode(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
-                         d.max_context_len, d.scale, 0, None, out, stream)
+                         d.max_context_len, d.scale, P, ws, None if P else out, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if P:
+            pa.pa_reduce(ws, d.context_lens, B, T * Hq, D, d.max_context_len, P, out, stream)
             if ev is not None:
-                ev[1].record(stream)
+                ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -221,11 +242,12 @@ def main() -> int:
         duration_source = "HIP events bracketing the K timed launches"
 
     ms_per_step = wall * 1e3 / args.steps
-    alg = w.algorithmic_bytes()
+    alg = w.algorithmic_bytes(query_tokens=T)
     value = alg / (ms_per_step * 1e-3) / 1e9
-    kbytes = decode_kernel_bytes(w, P)
+    kbytes = decode_kernel_bytes(w, P, T)
     achieved = kbytes / (decode_ms * 1e-3) / 1e9
-    traffic = stored_traffic(w.name, P)
+    workload = w.name + (f"-verify{T}" if args.verify else "")
+    traffic = stored_traffic(workload, P)
 
     rec = {
         "metric": "paged decode-attention KV GB/s and % of HBM peak; tokens/s at 70B-GQA 4K",
@@ -242,18 +264,18 @@ def main() -> int:
         "accum_dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name, "num_seqs": B, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
+            "workload": workload, "num_seqs": B, "query_tokens": T, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
             "head_dim": D, "max_context_len": w.max_context_len, "block_size": 16,
             "partition_size": P, "pool_blocks": w.num_blocks, "seed": args.seed if args.seed is not None else 1000 + args.config,
         },
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
-        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": alg,
         "device_us_per_step": round(device_ms_per_step * 1e3, 2),
         "decode_us": round(decode_ms * 1e3, 2),
         "reduce_us": round(reduce_ms * 1e3, 2),
         "roofline": {
-            "kernel": "pa_decode",
+            "kernel": "pa_verify_decode" if args.verify else "pa_decode",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -270,7 +292,7 @@ def main() -> int:
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host (cpu_baseline)")
-        rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"] = cpu_baseline(w, verify_q=q_np if args.verify else None)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -128,6 +128,31 @@ pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
                     int32_t max_context_len, float scale, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* out, hipStream_t stream);
 
+/* The verify step of speculative decoding: T = num_query_tokens draft tokens
+ * per sequence are scored in one call (the target model checks all of a draft
+ * model's candidates in one forward pass: §6.2 of the blog.tanteng.space page,
+ * §5.1 of the ialgorithm.me page; drafts of 4-8 tokens in "投机采样" of the
+ * ybb.press page).  The T draft tokens are the last T tokens of each context:
+ * their K/V are already in the pool (pa_write_kv) and context_lens[s] counts
+ * them.  Draft token i (0-based) of sequence s attends causally, to the tokens
+ * [0, context_lens[s] - T + 1 + i):
+ *   out[s][i][h] = softmax(scale * q[s][i][h] . K_s[0 .. lim)^T) V_s[0 .. lim).
+ * So row i equals what pa_decode returns for that token when the sequence is
+ * decoded one token at a time.  A row with lim <= 0 is zero.  q and out are
+ * [num_seqs][T][num_q_heads][head_dim] in the pool dtype; 1 <= T <= 256.  T = 1
+ * is pa_decode.  Split mode works as in pa_decode with T * num_q_heads rows
+ * per sequence: size the workspace with pa_decode_workspace_bytes(num_seqs,
+ * T * num_q_heads, ...) and merge with pa_reduce(..., T * num_q_heads, ...).
+ * The T * G rows of one KV head (G = num_q_heads / num_kv_heads) are computed
+ * together, so each K/V tile is read once for all draft tokens. */
+pa_status pa_verify_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                           int32_t max_context_len, float scale, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, void* out,
+                           hipStream_t stream);
+
 /* Log-sum-exp merge of the partials pa_decode wrote into `workspace` (same
  * num_seqs, num_q_heads, head_dim, max_context_len and partition_size):
  *   M = max_p lse_p,  LSE = M + ln sum_p exp(lse_p - M),

@@ -294,3 +294,65 @@ def scatter_blocks(k_pool, v_pool, block_ids, k_src, v_src):
             k_out[b] = k_src[i]
             v_out[b] = v_src[i]
     return k_out, v_out
+
+
+# --------------------------------------------------------------------------
+# speculative-decoding verify: T draft tokens per sequence in one call
+# [P1 SpeculativeDecoder listing: the target model runs once over the context
+#  followed by the draft tokens; P3 §6.2 and P4 §5.1: all candidates are
+#  checked in one forward pass]
+# --------------------------------------------------------------------------
+def draft_limit(L: int, T: int, i: int) -> int:
+    """Tokens draft token i (0-based) of a T-token draft sees when the draft is
+    the last T of the L context tokens: itself and everything before it."""
+    return min(max(L - T + 1 + i, 0), L)
+
+
+def paged_verify(q, k_pool, v_pool, block_tables, context_lens, scale, dtype) -> np.ndarray:
+    """out[s][i][h] = softmax(scale * q[s,i,h] K^T) V over the first
+    draft_limit(L_s, T, i) tokens of sequence s.  q is [B][T][H_q][d] (stored
+    form); returns float64 [B][T][H_q][d]; a row that sees no token is 0."""
+    B, T, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    scale64 = float(np.float32(scale))
+    out = np.zeros((B, T, Hq, d))
+    for s in range(B):
+        L = int(context_lens[s])
+        for g in range(Hkv):
+            K = widen(k_rows(k_pool, block_tables[s], L, g), dtype)
+            V = widen(v_rows(v_pool, block_tables[s], L, g), dtype)
+            for i in range(T):
+                lim = draft_limit(L, T, i)
+                for h in range(Hq):
+                    if _gqa_kv_head(h, Hq, Hkv) == g:
+                        out[s, i, h], _ = attend_range(widen(q[s, i, h], dtype), K[:lim], V[:lim],
+                                                       scale64)
+    return out
+
+
+def paged_verify_partials(q, k_pool, v_pool, block_tables, context_lens, scale, dtype,
+                          partition_size: int, max_context_len: int):
+    """Partition partials of paged_verify, rows ordered (s, i, h):
+    o_part [B][T * H_q][n_parts][d], lse_part [B][T * H_q][n_parts]; partition p
+    of draft token i covers tokens [pP, min(draft_limit, (p+1)P))."""
+    B, T, Hq, d = q.shape
+    Hkv = k_pool.shape[1]
+    P = num_partitions(max_context_len, partition_size)
+    scale64 = float(np.float32(scale))
+    o_part = np.zeros((B, T * Hq, P, d))
+    lse_part = np.full((B, T * Hq, P), -np.inf)
+    for s in range(B):
+        L = int(context_lens[s])
+        for g in range(Hkv):
+            K = widen(k_rows(k_pool, block_tables[s], L, g), dtype)
+            V = widen(v_rows(v_pool, block_tables[s], L, g), dtype)
+            for i in range(T):
+                lim = draft_limit(L, T, i)
+                for h in range(g * (Hq // Hkv), (g + 1) * (Hq // Hkv)):
+                    qv = widen(q[s, i, h], dtype)
+                    for p in range(P):
+                        lo, hi = p * partition_size, min(lim, (p + 1) * partition_size)
+                        if lo < hi:
+                            o_part[s, i * Hq + h, p], lse_part[s, i * Hq + h, p] = attend_range(
+                                qv, K[lo:hi], V[lo:hi], scale64)
+    return o_part, lse_part

@@ -8,6 +8,7 @@
 namespace {
 
 constexpr int kMaxReduceParts = 8192;  // partition weights staged in 32 KiB of LDS
+constexpr int kMaxQueryTokens = 256;   // draft tokens per sequence in one verify call
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
@@ -101,21 +102,31 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return rows * head_dim * sizeof(float) + rows * sizeof(float);
 }
 
-pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
-                    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                    int32_t max_context_len, float scale, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes, void* out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_verify_decode: T query tokens per sequence (T = 1: decode).
+pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_query_tokens,
+                        int32_t num_q_heads, int32_t max_context_len, float scale,
+                        int32_t partition_size, void* workspace, size_t workspace_bytes, void* out,
+                        hipStream_t stream) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARG;
+  if (num_query_tokens < 1 || num_query_tokens > kMaxQueryTokens) return PA_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * pa::kBlockSize)
     return PA_ERR_INVALID_ARG;
   if (partition_size < 0 || partition_size % pa::kBlockSize != 0) return PA_ERR_INVALID_ARG;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;  // grid z
+  // (query token, head) rows per KV head, at most 64 per workgroup: grid y
+  const int64_t rows = static_cast<int64_t>(num_query_tokens) * (num_q_heads / pool->num_kv_heads);
+  if (static_cast<int64_t>(pool->num_kv_heads) * ((rows + 63) / 64) > 65535) return PA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_tables, 4) ||
       !aligned(context_lens, 4))
     return PA_ERR_MISALIGNED;
@@ -128,6 +139,7 @@ pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
   a.context_lens = context_lens;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
+  a.num_query_tokens = num_query_tokens;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
   a.head_dim = pool->head_dim;
@@ -136,6 +148,7 @@ pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
   a.dtype = pool->dtype;
   a.scale = scale;
 
+  const int32_t row_heads = num_query_tokens * num_q_heads;  // output rows per sequence
   if (partition_size == 0) {
     if (!out) return PA_ERR_INVALID_ARG;
     if (!aligned(out, 16)) return PA_ERR_MISALIGNED;
@@ -147,18 +160,44 @@ pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
     a.write_partials = false;
     a.out = out;
   } else {
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
+    const size_t need = pa_decode_workspace_bytes(num_seqs, row_heads, pool->head_dim,
                                                   max_context_len, partition_size);
     if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
     a.partition_tokens = partition_size;
     a.num_parts = num_parts_for(max_context_len, partition_size);
     a.write_partials = true;
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * a.num_parts;
+    const size_t nrows = static_cast<size_t>(num_seqs) * row_heads * a.num_parts;
     a.o_part = static_cast<float*>(workspace);
-    a.lse_part = a.o_part + rows * pool->head_dim;
+    a.lse_part = a.o_part + nrows * pool->head_dim;
   }
   return from_hip(pa::launch_decode(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, void* out, hipStream_t stream) {
+  return decode_common(pool, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, 1, num_q_heads, max_context_len, scale, partition_size, workspace,
+                       workspace_bytes, out, stream);
+}
+
+pa_status pa_verify_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_query_tokens, int32_t num_q_heads,
+                           int32_t max_context_len, float scale, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, void* out,
+                           hipStream_t stream) {
+  return decode_common(pool, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_query_tokens, num_q_heads, max_context_len, scale,
+                       partition_size, workspace, workspace_bytes, out, stream);
 }
 
 pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,

@@ -1,12 +1,20 @@
 // Paged decode attention on the matrix cores (gfx950), all element types.
 //
-// Work unit.  A workgroup of kWaves wavefronts owns (sequence s, KV head g, a
-// chunk of up to 16 query heads of g's group, partition p).  The partition's
-// 16-token blocks are dealt round-robin to the waves; every wave streams its
-// blocks through registers, keeping the next block's K and V in flight while
-// the current one is consumed, and carries its own online-softmax state.  The
-// waves are merged at the end through LDS with the log-sum-exp algebra, in a
-// fixed order (no atomics: runs are bit-reproducible).
+// Rows.  A query row is one (query token, query head) pair.  Decode has one
+// query token per sequence; the verify step of speculative decoding has T
+// draft tokens, the last T tokens of the context, and draft token i sees the
+// tokens [0, L - T + 1 + i) only (causal inside the draft).  The T * G rows of a
+// sequence that share KV head g (G = query heads per KV head) read the same K/V
+// tiles, so they are computed together: 16 rows per matrix-core chunk, up to
+// kChunks = 4 chunks per workgroup, and each tile is loaded once for all of them.
+//
+// Work unit.  A workgroup of kWaves wavefronts owns (sequence s, KV head g, up
+// to 16 * kChunks of g's rows, partition p).  The partition's 16-token blocks
+// are dealt round-robin to the waves; every wave streams its blocks through
+// registers, keeping the next block's K and V in flight while the current one
+// is consumed, and carries its own online-softmax state per row.  The waves
+// are merged at the end through LDS with the log-sum-exp algebra, in a fixed
+// order (no atomics: runs are bit-reproducible).
 //
 // Per 16-token block, everything is two small matrix products whose operands
 // come straight from the loads (lane l: r = l % 16, q = l / 16):
@@ -16,9 +24,9 @@
 //               per 16 bytes), so load j of a tile is the contiguous 1 KiB
 //               tile[64 j + lane] = chunk 4j + q of token r: exactly lane l's
 //               A operand of step j.
-//           B = Q: lane l holds chunk 4j + q of query head r (zero rows pad the
-//               group to 16).
-//           out: lane l holds the logits of tokens 4q .. 4q+3 for head r.
+//           B = Q: lane l holds chunk 4j + q of query row r of the chunk (zero
+//               rows pad the chunk to 16).
+//           out: lane l holds the logits of tokens 4q .. 4q+3 for row r.
 //   P.V     O^T[col][head] += V^T[col][token] . P^T[token][head]   (16 x 16 x 16 per 16 columns)
 //           A = V tile: the pool stores V head-dim-major ([d][16]), so lane l's
 //               operand (tokens 4q .. 4q+3 of column 16 cb + r) is one
@@ -26,11 +34,11 @@
 //               contiguous elements.
 //           B = P: lane l already holds the weights of tokens 4q .. 4q+3 for
 //               head r -- the logits' own output layout -- so P never moves.
-//           out: lane l holds O[head r][16 cb + 4q .. 16 cb + 4q + 3].
+//           out: lane l holds O[row r][16 cb + 4q .. 16 cb + 4q + 3].
 //
 // Online softmax (§4.2 of the ialgorithm.me page: the normaliser is updated
-// while streaming, exactly): the running maximum m of each head is shared by
-// the four lanes holding that head (two lane-swap max steps per block).  m is
+// while streaming, exactly): the running maximum m of each row is shared by
+// the four lanes holding that row (two lane-swap max steps per block).  m is
 // only raised when a block's maximum exceeds it by more than kSlack (log2
 // units); until then weights up to 2^kSlack are accumulated as they are.  The
 // result is the same algebra (every partial sum uses one common reference), and
@@ -38,9 +46,12 @@
 // element type for the matrix product and the running sum adds exactly the
 // rounded values, so out is a true convex combination of V rows.
 //
-// Partial blocks: the rows past the context end of a block may hold anything
-// (NaN included); their logits are selected to -inf and their V elements to 0
-// before any arithmetic touches them.
+// Partial blocks: the token slots past the context end of a block may hold
+// anything (NaN included); their logits are selected to -inf and their V
+// elements to 0 before any arithmetic touches them.  Draft rows mask the
+// tokens past their own limit the same way (those V elements are real values
+// and meet weight 0).  A row that has seen no token keeps m = -inf and
+// contributes nothing.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -204,7 +215,7 @@ __device__ __forceinline__ float sum_over_q(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <class M, class Tr, int D, int kWaves>
+template <class M, class Tr, int D, int kWaves, int kChunks>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   constexpr int kKLoads = D * M::kBytes / 64;  // 1 KiB K loads per tile (= 16-byte chunks / 4)
   constexpr int kColBlocks = D / 16;           // P.V output blocks of 16 columns
@@ -220,12 +231,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int qg = lane >> 4;
   const int wave = wave_id();
   const int part = blockIdx.x;
+  const int T = a.num_query_tokens;
   const int group = a.num_q_heads / a.num_kv_heads;
-  const int chunks = (group + 15) / 16;
-  const int g = blockIdx.y / chunks;
-  const int hc = blockIdx.y % chunks;
-  const int h0 = g * group + hc * 16;
-  const int nh = min(16, group - hc * 16);  // live query heads in this chunk
+  const int rows = T * group;  // (query token, query head) rows that read KV head g
+  const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
+  const int g = blockIdx.y / wgs;
+  const int row0 = (blockIdx.y % wgs) * (16 * kChunks);
   const int s = blockIdx.z;
 
   const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
@@ -233,26 +244,44 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int t_hi = min(L, t_lo + a.partition_tokens);
   const int blk_lo = t_lo / kBlockSize;
   const int blk_hi = t_hi > t_lo ? (t_hi + kBlockSize - 1) / kBlockSize : blk_lo;
+  // Query token i sees the tokens [0, L - T + 1 + i) (the draft is causal; one
+  // query token sees the whole context).  Blocks that end past the smallest
+  // limit of this workgroup's rows are masked row by row.
+  const int t_hi_min = min(t_hi, L - T + 1 + row0 / group);
 
-  // B operand of the logits: chunk 4j + qg of query head h0 + r (zero padding rows)
-  uint4 qop[kKLoads];
-  {
-    const int hq = h0 + min(r, nh - 1);  // padding rows read a live row, then drop it
+  // Per chunk c, lane l holds row row0 + 16 c + r: the B operand of its logits
+  // (chunk 4j + qg of that row's query vector, zero for padding rows), its token
+  // limit, and its online-softmax state.
+  uint4 qop[kChunks][kKLoads];
+  int row_hi[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int rho = row0 + 16 * c + r;
+    const bool live = rho < rows;
+    const int rr = live ? rho : rows - 1;  // padding rows read a live row, then drop it
+    const int i = rr / group;
+    const int hq = g * group + rr % group;
     const char* qrow = static_cast<const char*>(a.q) +
-                       (static_cast<size_t>(s) * a.num_q_heads + hq) * D * M::kBytes;
+                       ((static_cast<size_t>(s) * T + i) * a.num_q_heads + hq) * D * M::kBytes;
 #pragma unroll
     for (int j = 0; j < kKLoads; ++j) {
       const uint4 v = reinterpret_cast<const uint4*>(qrow)[4 * j + qg];
-      qop[j] = r < nh ? v : make_uint4(0u, 0u, 0u, 0u);
+      qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
     }
+    row_hi[c] = live ? min(t_hi, L - T + 1 + i) : t_hi;
   }
   const float qs = a.scale * kLog2e;  // logits in log2 units
 
-  float m = -INFINITY;  // running maximum (log2 units) of head r, shared by its 4 lanes
-  float lsum = 0.f;     // this lane's share of the running sum
-  f32x4 acc[kColBlocks];
+  float m[kChunks];     // running maximum (log2 units) of row r, shared by its 4 lanes
+  float lsum[kChunks];  // this lane's share of the running sum
+  f32x4 acc[kChunks][kColBlocks];
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < kChunks; ++c) {
+    m[c] = -INFINITY;
+    lsum[c] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb) acc[c][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int32_t* __restrict__ trow = a.block_tables + static_cast<size_t>(s) * a.max_blocks_per_seq;
   const char* __restrict__ kbase = static_cast<const char*>(a.k_pool);
@@ -272,37 +301,44 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   };
 
   auto consume = [&](int jb, const uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < kKLoads; ++j) sc = M::qk(kr[j], qop[j], sc);
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs;
     const int tok0 = jb * kBlockSize + 4 * qg;  // first token of this lane's four
-    if ((jb + 1) * kBlockSize > t_hi) {          // partial block (wave-uniform test)
+    if ((jb + 1) * kBlockSize > t_hi) {          // V rows past the partition (wave-uniform test)
       const int n = min(max(t_hi - tok0, 0), 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i >= n) x[i] = -INFINITY;
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) M::keep(vr[cb], n);
     }
-    const float bmax = max_over_q(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    const bool raise = bmax > m + kSlack;
-    if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform
-      const float mn = raise ? bmax : m;
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block, 1 if kept
-      m = mn;
-      lsum *= alpha;
+    const bool masked = (jb + 1) * kBlockSize > t_hi_min;  // wave-uniform
 #pragma unroll
-      for (int cb = 0; cb < kColBlocks; ++cb) acc[cb] *= alpha;
+    for (int c = 0; c < kChunks; ++c) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kKLoads; ++j) sc = M::qk(kr[j], qop[c][j], sc);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs;
+      if (masked) {
+        const int n = min(max(row_hi[c] - tok0, 0), 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i >= n) x[i] = -INFINITY;
+      }
+      const float bmax = max_over_q(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      const bool raise = bmax > m[c] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m[c] - bmax) : 1.f;  // 0 on a first block
+        m[c] = raise ? bmax : m[c];
+        lsum[c] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb) acc[c][cb] *= alpha;
+      }
+      const float mref = m[c] == -INFINITY ? 0.f : m[c];  // a row that has seen no token yet
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+      const typename M::POp pop = M::pack(p, lsum[c]);
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) acc[c][cb] = M::pv(vr[cb], pop, acc[c][cb]);
     }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m);
-    const typename M::POp pop = M::pack(p, lsum);
-#pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) acc[cb] = M::pv(vr[cb], pop, acc[cb]);
   };
 
   // A ring of kDepth register sets: the wave's i-th block (logical block
@@ -341,42 +377,48 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     if (done) break;
   }
 
-  // this wave's results -> LDS
-  lsum = sum_over_q(lsum);
+  // merge the waves through LDS, one chunk of 16 rows at a time, and write
 #pragma unroll
-  for (int cb = 0; cb < kColBlocks; ++cb)
-    *reinterpret_cast<f32x4*>(&sm_o[wave][r][16 * cb + 4 * qg]) = acc[cb];
-  if (qg == 0) {
-    sm_m[wave][r] = m;
-    sm_l[wave][r] = lsum;
-  }
-  __syncthreads();
-
-  // merge the waves and write
-  for (int idx = threadIdx.x; idx < nh * D; idx += kWaves * 64) {
-    const int h = idx / D;
-    const int c = idx % D;
-    float M_ = -INFINITY;
+  for (int c = 0; c < kChunks; ++c) {
+    const int nh = min(16, rows - (row0 + 16 * c));  // live rows of this chunk
+    if (nh <= 0) break;                              // workgroup-uniform
+    const float ls = sum_over_q(lsum[c]);
+    if (c > 0) __syncthreads();  // the previous chunk's merge has read LDS
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, sm_m[w][h]);
-    float o = 0.f, lse = -INFINITY;
-    if (M_ != -INFINITY) {
-      float ls = 0.f, os = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M_);  // 0 for an idle wave
-        ls = fmaf(sm_l[w][h], f, ls);
-        os = fmaf(sm_o[w][h][c], f, os);
-      }
-      o = os / ls;
-      lse = (M_ + __log2f(ls)) * kLn2;
+    for (int cb = 0; cb < kColBlocks; ++cb)
+      *reinterpret_cast<f32x4*>(&sm_o[wave][r][16 * cb + 4 * qg]) = acc[c][cb];
+    if (qg == 0) {
+      sm_m[wave][r] = m[c];
+      sm_l[wave][r] = ls;
     }
-    const size_t row = static_cast<size_t>(s) * a.num_q_heads + h0 + h;
-    if (a.write_partials) {
-      a.o_part[(row * a.num_parts + part) * D + c] = o;
-      if (c == 0) a.lse_part[row * a.num_parts + part] = lse;
-    } else {
-      Tr::store(a.out, row * D + c, o);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nh * D; idx += kWaves * 64) {
+      const int h = idx / D;
+      const int col = idx % D;
+      float M_ = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, sm_m[w][h]);
+      float o = 0.f, lse = -INFINITY;
+      if (M_ != -INFINITY) {
+        float lsw = 0.f, os = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M_);  // 0 for an idle wave
+          lsw = fmaf(sm_l[w][h], f, lsw);
+          os = fmaf(sm_o[w][h][col], f, os);
+        }
+        o = os / lsw;
+        lse = (M_ + __log2f(lsw)) * kLn2;
+      }
+      const int rho = row0 + 16 * c + h;
+      const size_t row = (static_cast<size_t>(s) * T + rho / group) * a.num_q_heads +
+                         g * group + rho % group;
+      if (a.write_partials) {
+        a.o_part[(row * a.num_parts + part) * D + col] = o;
+        if (col == 0) a.lse_part[row * a.num_parts + part] = lse;
+      } else {
+        Tr::store(a.out, row * D + col, o);
+      }
     }
   }
 }
@@ -386,16 +428,39 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 // evenly); shorter ones get 4.
 constexpr int kWideTokens = 4096;
 
+// Row chunks per workgroup: every (query token, query head) row of one KV head
+// in one workgroup when there are at most 64, so each K/V tile is read once.
+int chunks_for(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+
+template <class M, class Tr, int D, int kChunks>
+hipError_t launch_c(const DecodeArgs& a, hipStream_t stream) {
+  const int rows = a.num_query_tokens * (a.num_q_heads / a.num_kv_heads);
+  const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
+  dim3 grid(a.num_parts, a.num_kv_heads * wgs, a.num_seqs);
+  // Four chunks hold 64 rows of state per lane: only 4 waves per workgroup fit
+  // them without spilling.
+  if constexpr (kChunks < 4) {
+    if (a.partition_tokens >= kWideTokens) {
+      hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks>), grid, dim3(8 * 64), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks>), grid, dim3(4 * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <class M, class Tr, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int chunks = (group + 15) / 16;
-  dim3 grid(a.num_parts, a.num_kv_heads * chunks, a.num_seqs);
-  if (a.partition_tokens >= kWideTokens)
-    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8>), grid, dim3(8 * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4>), grid, dim3(4 * 64), 0, stream, a);
-  return hipGetLastError();
+  if constexpr (M::kBytes == 4 && D == 128) {
+    // an 8 KiB float32 tile fills the registers already: one chunk per workgroup
+    return launch_c<M, Tr, D, 1>(a, stream);
+  } else {
+    switch (chunks_for(a.num_query_tokens * (a.num_q_heads / a.num_kv_heads))) {
+      case 1: return launch_c<M, Tr, D, 1>(a, stream);
+      case 2: return launch_c<M, Tr, D, 2>(a, stream);
+      default: return launch_c<M, Tr, D, 4>(a, stream);
+    }
+  }
 }
 
 template <class M, class Tr>

@@ -19,6 +19,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   int32_t max_blocks_per_seq;
   int32_t num_seqs;
+  int32_t num_query_tokens;  // query tokens per sequence: 1 (decode) or T (verify)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;

@@ -30,7 +30,7 @@ BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_init_pool", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
-           "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
+           "pa_verify_decode", "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
            "pa_scatter_blocks", "pa_status_string")
 
 
@@ -72,6 +72,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32, ctypes.c_float, i32,
                               vp, sz, vp, vp]
+    lib.pa_verify_decode.restype = ctypes.c_int
+    lib.pa_verify_decode.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                     ctypes.c_float, i32, vp, sz, vp, vp]
     lib.pa_reduce.restype = ctypes.c_int
     lib.pa_reduce.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_debug_slot_ids.restype = ctypes.c_int
@@ -149,6 +152,19 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: in
         float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
 
 
+def pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                     scale: float, partition_size: int = 0, workspace=None, out=None,
+                     stream=None) -> None:
+    """q and out: [B][T][H_q][d] (T draft tokens per sequence)."""
+    desc = pool_desc(k_pool)
+    B, T, Hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_verify_decode", load().pa_verify_decode(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq, int(max_context_len),
+        float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
+
+
 def pa_reduce(workspace, context_lens, num_seqs: int, num_q_heads: int, head_dim: int,
               max_context_len: int, partition_size: int, out, stream=None) -> None:
     _check("pa_reduce", load().pa_reduce(
@@ -214,4 +230,25 @@ def paged_attention(q, k_pool, v_pool, block_tables, context_lens, max_context_l
     else:
         pa_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale, 0, None,
                   out, stream)
+    return out
+
+
+def verify_attention(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                     scale: float, partition_size: int = 0, workspace=None, out=None, stream=None):
+    """out = pa_verify_decode (+ pa_reduce over T * H_q rows when split).  q is
+    [B][T][H_q][d]; returns out of the same shape."""
+    if out is None:
+        out = torch.empty_like(q)
+    B, T, Hq, D = q.shape
+    if partition_size > 0:
+        if workspace is None:
+            n = pa_decode_workspace_bytes(B, T * Hq, D, max_context_len, partition_size)
+            workspace = torch.empty(n // 4, dtype=torch.float32, device=q.device)
+        pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
+                         partition_size, workspace, None, stream)
+        pa_reduce(workspace, context_lens, B, T * Hq, D, max_context_len, partition_size, out,
+                  stream)
+    else:
+        pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale, 0,
+                         None, out, stream)
     return out

@@ -167,10 +167,12 @@ class Workload:
             return int(shared + (lens - shared).sum()) * per_token
         return int(lens.sum()) * per_token
 
-    def algorithmic_bytes(self, unique: bool = False) -> int:
-        """KV + q + out + live block-table entries + context_lens."""
+    def algorithmic_bytes(self, unique: bool = False, query_tokens: int = 1) -> int:
+        """KV + q + out + live block-table entries + context_lens (q and out hold
+        ``query_tokens`` rows per sequence and head: 1 for decode, T for a verify
+        call over a T-token draft)."""
         e = ELEM_BYTES[self.dtype]
-        qo = 2 * self.num_seqs * self.num_q_heads * self.head_dim * e
+        qo = 2 * query_tokens * self.num_seqs * self.num_q_heads * self.head_dim * e
         live_entries = int(((self.context_lens.astype(np.int64) + BLOCK_SIZE - 1) // BLOCK_SIZE).sum())
         kv = self.kv_bytes_unique() if unique else self.kv_bytes_logical()
         return kv + qo + 4 * live_entries + 4 * self.num_seqs

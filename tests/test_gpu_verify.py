@@ -1,0 +1,127 @@
+"""GPU parity of the speculative-decoding verify call (``pa_verify_decode``):
+T draft tokens per sequence, causal inside the draft, against the fp64 oracle
+(``oracle.paged_verify``) through the C ABI.
+
+Also checked: draft row i equals what ``pa_decode`` returns when the sequence
+is decoded one token at a time (context cut to L - T + 1 + i) -- the property
+that makes verification lossless -- to within one unit in the last place of
+the output type.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_365_amd import pa
+from paged_kv_cache_365_amd import workloads as wl
+from paged_kv_cache_365_amd.device import to_torch, upload, widen_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+LSE_TOL = {"f32": 1e-4, "f16": 2.0 ** -11 + 1e-4, "bf16": 2.0 ** -8 + 1e-4}
+ULP_BITS = {"f32": 23, "f16": 10, "bf16": 7}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pa.load()
+
+
+def queries(seed, B, T, Hq, d, dtype):
+    return wl.normal(np.random.default_rng(seed), (B, T, Hq, d), dtype)
+
+
+def assert_close(got, want, tol, what):
+    err = np.abs(got - want)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert err.max(initial=0.0) <= tol, f"{what}: max-abs {err.max():.3e} > {tol}"
+
+
+CASES = [
+    # dtype, d, Hq, Hkv, T, partition
+    ("bf16", 128, 64, 8, 4, 0), ("bf16", 128, 64, 8, 2, 32), ("bf16", 128, 32, 8, 8, 0),
+    ("bf16", 128, 16, 2, 5, 16), ("f16", 128, 8, 8, 4, 0), ("f16", 64, 16, 1, 3, 0),
+    ("f16", 128, 32, 4, 8, 48), ("f32", 64, 8, 2, 4, 0), ("f32", 128, 8, 4, 2, 16),
+    ("bf16", 64, 64, 1, 1, 0), ("bf16", 128, 128, 2, 1, 32), ("f32", 64, 4, 4, 6, 32),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_verify_random_cases(case):
+    dtype, d, hq, hkv, T, P = CASES[case]
+    lens = [1, 2, T, T + 1, 15, 16, 17, 63, 150, 300]
+    w = wl.make_random_case(800 + case, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=d, dtype=dtype, lens=lens)
+    dw = upload(w, DEV)
+    q = queries(900 + case, len(lens), T, hq, d, dtype)
+    tq = to_torch(q, dtype, DEV)
+    out = torch.empty_like(tq)
+    ws = None
+    if P:
+        n = pa.pa_decode_workspace_bytes(len(lens), T * hq, d, w.max_context_len, P)
+        ws = torch.empty(n // 4, dtype=torch.float32, device=DEV)
+    pa.verify_attention(tq, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+                        w.max_context_len, w.scale, partition_size=P, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    want = oracle.paged_verify(q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale, dtype)
+    assert_close(widen_f32(out), want, TOL[dtype], f"{CASES[case]}")
+    if P:
+        n_parts = oracle.num_partitions(w.max_context_len, P)
+        rows = len(lens) * T * hq
+        wsn = ws.cpu().numpy()
+        o_p = wsn[: rows * n_parts * d].reshape(len(lens), T * hq, n_parts, d).astype(np.float64)
+        lse_p = wsn[rows * n_parts * d: rows * n_parts * (d + 1)].reshape(len(lens), T * hq, n_parts)
+        wo, wlse = oracle.paged_verify_partials(q, w.k_pool, w.v_pool, w.block_tables,
+                                                w.context_lens, w.scale, dtype, P, w.max_context_len)
+        live = np.isfinite(wlse)
+        assert np.array_equal(np.isfinite(lse_p), live), "empty partitions must be -inf"
+        assert np.abs(lse_p[live] - wlse[live]).max(initial=0) <= LSE_TOL[dtype]
+        assert_close(o_p[live], wo[live], TOL[dtype], "partials")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,T,P", [("bf16", 64, 8, 4, 0), ("f16", 16, 2, 3, 32),
+                                              ("f32", 8, 2, 2, 0)])
+def test_verify_row_equals_sequential_decode(dtype, hq, hkv, T, P):
+    lens = [T, 20, 64, 100, 257]
+    d = 128 if dtype != "f32" else 64
+    w = wl.make_random_case(950, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=d, dtype=dtype, lens=lens)
+    dw = upload(w, DEV)
+    q = queries(951, len(lens), T, hq, d, dtype)
+    tq = to_torch(q, dtype, DEV)
+    out = pa.verify_attention(tq, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
+                              w.max_context_len, w.scale, partition_size=P)
+    torch.cuda.synchronize()
+    ver = widen_f32(out)
+    for i in range(T):
+        lens_i = torch.tensor([oracle.draft_limit(L, T, i) for L in lens], dtype=torch.int32,
+                              device=DEV)
+        one = pa.paged_attention(tq[:, i].contiguous(), dw.k_pool, dw.v_pool, dw.block_tables,
+                                 lens_i, w.max_context_len, w.scale, partition_size=P)
+        torch.cuda.synchronize()
+        seq = widen_f32(one)
+        ulp = np.maximum(np.abs(seq), 2.0 ** -14) * 2.0 ** -ULP_BITS[dtype]
+        assert (np.abs(ver[:, i] - seq) <= ulp).all(), f"draft row {i}"
+
+
+def test_verify_70b_gqa_4k_draft4_sampled():
+    """The 70B-style batch (64 x 4096 tokens, 64/8 heads, bf16) verifying a
+    4-token draft, at full size, in the launch configuration the benchmark
+    uses; sampled rows against the oracle."""
+    w = wl.make_config(2)
+    dw = upload(w, DEV)
+    T = 4
+    q = queries(2002, w.num_seqs, T, w.num_q_heads, w.head_dim, w.dtype)
+    out = pa.verify_attention(to_torch(q, w.dtype, DEV), dw.k_pool, dw.v_pool, dw.block_tables,
+                              dw.context_lens, w.max_context_len, w.scale)
+    torch.cuda.synchronize()
+    got = widen_f32(out)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(3)
+    for s in sorted(set(rng.integers(0, w.num_seqs, size=6).tolist()) | {0, w.num_seqs - 1}):
+        want = oracle.paged_verify(q[s:s + 1], w.k_pool, w.v_pool, w.block_tables[s:s + 1],
+                                   w.context_lens[s:s + 1], w.scale, w.dtype)[0]
+        heads = [0, 7, 8, 63]
+        assert_close(got[s][:, heads], want[:, heads], TOL[w.dtype], f"seq {s}")

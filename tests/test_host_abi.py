@@ -132,3 +132,20 @@ def test_block_moves_reject_bad_arguments(lib):
     assert g(ctypes.byref(d), FAKE, FAKE, FAKE, 2, FAKE + 4, FAKE, None) == pa.PA_ERR_MISALIGNED
     assert s(ctypes.byref(d), FAKE, FAKE, FAKE, -3, FAKE, FAKE, None) == pa.PA_ERR_INVALID_ARG
     assert s(ctypes.byref(d), FAKE, FAKE, FAKE + 2, 2, FAKE, FAKE, None) == pa.PA_ERR_MISALIGNED
+
+
+def test_verify_rejects_bad_arguments(lib):
+    d = _desc()
+    v = lib.pa_verify_decode
+
+    def call(T=4, Hq=4, P=0, ws=None, ws_bytes=0, out=FAKE, q=FAKE):
+        return v(ctypes.byref(d), q, FAKE, FAKE, FAKE, 4, FAKE, 2, T, Hq, 40, 0.125, P, ws,
+                 ws_bytes, out, None)
+    assert call(T=0) == pa.PA_ERR_INVALID_ARG
+    assert call(T=257) == pa.PA_ERR_INVALID_ARG
+    assert call(Hq=3) == pa.PA_ERR_INVALID_ARG
+    assert call(out=None) == pa.PA_ERR_INVALID_ARG
+    assert call(q=FAKE + 2) == pa.PA_ERR_MISALIGNED
+    # split mode needs room for T * H_q rows per sequence
+    need = pa.pa_decode_workspace_bytes(2, 4 * 4, 64, 40, 16)
+    assert call(P=16, ws=FAKE, ws_bytes=need - 4) == pa.PA_ERR_WORKSPACE

@@ -36,6 +36,9 @@ MUTATIONS = {
                      "lo, hi = p * partition_size, min(L, (p + 1) * partition_size - 1)"),
     "tile_off": ("return (physical * num_kv_heads + kv_head) * tile_bytes",
                  "return (physical + kv_head * num_kv_heads) * tile_bytes"),
+    "draft_limit_excludes_self": ("return min(max(L - T + 1 + i, 0), L)", "return min(max(L - T + i, 0), L)"),
+    "draft_limit_reversed": ("lim = draft_limit(L, T, i)\n                for h in range(Hq):",
+                             "lim = draft_limit(L, T, T - 1 - i)\n                for h in range(Hq):"),
     "widen_f16_as_bf16": ('        return np.asarray(x, dtype=np.float16).astype(np.float64)',
                           '        return (np.asarray(x, dtype=np.float16).view(np.uint16).astype(np.uint32)'
                           ' << np.uint32(16)).view(np.float32).astype(np.float64)'),

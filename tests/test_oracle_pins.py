@@ -524,6 +524,88 @@ def test_gather_scatter_round_trip_is_a_relabelling(dtype):
 
 
 # ---------------------------------------------------------------------------
+# speculative-decoding verify: T draft tokens, causal inside the draft
+# ---------------------------------------------------------------------------
+def causal_brute_force(Qd, K, V, scale):
+    """Dense causal attention of the last T positions of a context, written here:
+    Qd [T][H_q][d], K and V [L][H_kv][d] (float64).  Position L - T + i may attend
+    to keys 0 .. L - T + i; the mask matrix is built explicitly and the softmax is
+    scipy's."""
+    from scipy.special import softmax
+    T, Hq, d = Qd.shape
+    L, Hkv, _ = K.shape
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, d))
+    pos = np.arange(L - T, L)                               # query positions
+    mask = np.where(np.arange(L)[None, :] <= pos[:, None], 0.0, -np.inf)
+    for h in range(Hq):
+        logits = Qd[:, h, :] @ K[:, h // G, :].T * scale + mask   # [T][L]
+        w = softmax(logits, axis=-1)
+        out[:, h, :] = w @ V[:, h // G, :]
+    return out
+
+
+@pytest.mark.parametrize("T,G,L", [(4, 8, 37), (2, 1, 16), (5, 4, 80), (8, 2, 9), (3, 16, 3)])
+def test_verify_equals_causal_brute_force(T, G, L):
+    rng = np.random.default_rng(74 + T)
+    Hkv, d = 2, 64
+    Hq = Hkv * G
+    K = f32_normal(rng, (1, L, Hkv, d))
+    V = f32_normal(rng, (1, L, Hkv, d))
+    Q = f32_normal(rng, (1, T, Hq, d))
+    kp, vp, tab = scatter_to_pool(K, V, [L], rng)
+    got = oracle.paged_verify(Q, kp, vp, tab, np.array([L]), 0.125, "f32")[0]
+    want = causal_brute_force(Q[0].astype(np.float64), K[0].astype(np.float64),
+                              V[0].astype(np.float64), 0.125)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_verify_with_one_token_is_decode():
+    rng = np.random.default_rng(75)
+    w = wl.make_random_case(75, num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                            dtype="bf16", lens=[1, 16, 33, 70])
+    got = oracle.paged_verify(w.q[:, None], w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                              w.scale, w.dtype)[:, 0]
+    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                               w.dtype)
+    assert np.array_equal(got, want)
+    del rng
+
+
+def test_verify_short_contexts_and_first_row():
+    """A context shorter than the draft: rows that see no token are zero; the
+    first draft row of an L = T context sees exactly one token and returns v0."""
+    rng = np.random.default_rng(76)
+    T, Hkv, G, d = 4, 1, 2, 64
+    K = f32_normal(rng, (1, 4, Hkv, d))
+    V = f32_normal(rng, (1, 4, Hkv, d))
+    Q = f32_normal(rng, (1, T, Hkv * G, d))
+    kp, vp, tab = scatter_to_pool(K, V, [4], rng)
+    out = oracle.paged_verify(Q, kp, vp, tab, np.array([2]), 0.125, "f32")[0]
+    assert not out[:2].any()                                  # limits 2-4+1+0 = -1 and 0
+    assert np.array_equal(out[2, 0], V[0, 0, 0].astype(np.float64))
+    out4 = oracle.paged_verify(Q, kp, vp, tab, np.array([4]), 0.125, "f32")[0]
+    assert np.array_equal(out4[0, 1], V[0, 0, 0].astype(np.float64))
+    assert [oracle.draft_limit(4, 4, i) for i in range(4)] == [1, 2, 3, 4]
+
+
+@pytest.mark.parametrize("P", [16, 32])
+def test_verify_partials_merge_to_verify(P):
+    rng = np.random.default_rng(77)
+    T, Hkv, G, d = 3, 2, 4, 64
+    lens = [2, 17, 50]
+    Lmax = max(lens)
+    K = f32_normal(rng, (3, Lmax, Hkv, d))
+    V = f32_normal(rng, (3, Lmax, Hkv, d))
+    Q = f32_normal(rng, (3, T, Hkv * G, d))
+    kp, vp, tab = scatter_to_pool(K, V, lens, rng)
+    o, lse = oracle.paged_verify_partials(Q, kp, vp, tab, np.array(lens), 0.125, "f32", P, Lmax)
+    merged = oracle.merge_partials(o, lse).reshape(3, T, Hkv * G, d)
+    want = oracle.paged_verify(Q, kp, vp, tab, np.array(lens), 0.125, "f32")
+    np.testing.assert_allclose(merged, want, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # the dense brute force itself, against closed forms
 # ---------------------------------------------------------------------------
 def test_dense_closed_forms():
