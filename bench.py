@@ -30,14 +30,17 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+DECODE_SOURCES = ("pa_decode.hip", "pa_common.h", "pa_internal.h")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the decode kernel sources, to tell whether stored counters still apply."""
+    """Hash of the sources the decode kernel is compiled from, to tell whether
+    stored counters still apply."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_365_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in DECODE_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 

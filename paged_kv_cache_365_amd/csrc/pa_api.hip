@@ -123,10 +123,12 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * pa::kBlockSize)
     return PA_ERR_INVALID_ARG;
   if (partition_size < 0 || partition_size % pa::kBlockSize != 0) return PA_ERR_INVALID_ARG;
-  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;  // grid z
-  // (query token, head) rows per KV head, at most 64 per workgroup: grid y
+  // one workgroup per 16 (query token, head) rows at most, per KV head, sequence
+  // and partition: the one-dimensional grid must count them in 31 bits
   const int64_t rows = static_cast<int64_t>(num_query_tokens) * (num_q_heads / pool->num_kv_heads);
-  if (static_cast<int64_t>(pool->num_kv_heads) * ((rows + 63) / 64) > 65535) return PA_ERR_UNSUPPORTED;
+  const int64_t parts = partition_size > 0 ? num_parts_for(max_context_len, partition_size) : 1;
+  if (static_cast<int64_t>(num_seqs) * pool->num_kv_heads * ((rows + 15) / 16) * parts > INT32_MAX)
+    return PA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_tables, 4) ||
       !aligned(context_lens, 4))
     return PA_ERR_MISALIGNED;

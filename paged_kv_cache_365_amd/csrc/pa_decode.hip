@@ -5,8 +5,10 @@
 // draft tokens, the last T tokens of the context, and draft token i sees the
 // tokens [0, L - T + 1 + i) only (causal inside the draft).  The T * G rows of a
 // sequence that share KV head g (G = query heads per KV head) read the same K/V
-// tiles, so they are computed together: 16 rows per matrix-core chunk, up to
-// kChunks = 4 chunks per workgroup, and each tile is loaded once for all of them.
+// tiles, so they are computed together: 16 rows per matrix-core chunk, kChunks
+// chunks per workgroup (two at most), and each tile is loaded once for all of
+// them.  More rows than that go to sibling workgroups placed on one XCD, which
+// read the tiles through that XCD's L2 (see unit_of).
 //
 // Work unit.  A workgroup of kWaves wavefronts owns (sequence s, KV head g, up
 // to 16 * kChunks of g's rows, partition p).  The partition's 16-token blocks
@@ -103,8 +105,6 @@ __device__ __forceinline__ T load16(const T* p) {
     return *p;
   }
 }
-constexpr bool kStreamK = PA_DECODE_NT == 1 || PA_DECODE_NT == 2;
-constexpr bool kStreamV = PA_DECODE_NT == 1 || PA_DECODE_NT == 3;
 
 // ---------------------------------------------------------------------------
 // element-type specific operand handling
@@ -215,8 +215,45 @@ __device__ __forceinline__ float sum_over_q(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <class M, class Tr, int D, int kWaves, int kChunks>
+// Work unit of a workgroup.  The grid is one-dimensional; units are numbered
+// sibling-fastest, then partition, KV head, sequence: n = ((s * H_kv + g) *
+// parts + p) * wgs + w, where the wgs siblings w split the rows of one
+// (s, g, p) and read the same K/V tiles.  Workgroups are handed to the 8 XCDs
+// round-robin (workgroup i to XCD i mod 8), and each XCD has its own L2, so
+// when there are siblings the ids are permuted to put all siblings of a unit
+// on one XCD, dispatched back to back: the tiles the first one brings into
+// that L2 serve the others.  Without siblings the numbering is the identity.
+struct Unit {
+  int sibling, part, kv_head, seq;
+};
+__device__ __forceinline__ Unit unit_of(int id, int total, int wgs, int parts, int kv_heads) {
+  constexpr int kXcds = 8;
+  int n = id;
+  if (wgs > 1) {
+    const int span = kXcds * wgs;
+    const int whole = total / span * span;  // the tail past whole multiples keeps its ids
+    if (id < whole) {
+      const int xcd = id % kXcds;
+      const int slot = id / kXcds;  // position in this XCD's dispatch order
+      n = ((slot / wgs) * kXcds + xcd) * wgs + slot % wgs;
+    }
+  }
+  Unit u;
+  u.sibling = n % wgs;
+  n /= wgs;
+  u.part = n % parts;
+  n /= parts;
+  u.kv_head = n % kv_heads;
+  u.seq = n / kv_heads;
+  return u;
+}
+
+template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
+  // Sibling workgroups (kShared) read each tile through the XCD's L2 one after
+  // another, so their loads must not carry the streaming hint.
+  constexpr bool kStreamK = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 2);
+  constexpr bool kStreamV = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 3);
   constexpr int kKLoads = D * M::kBytes / 64;  // 1 KiB K loads per tile (= 16-byte chunks / 4)
   constexpr int kColBlocks = D / 16;           // P.V output blocks of 16 columns
   constexpr int kPad = 4;                      // LDS row padding (floats)
@@ -230,14 +267,15 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int r = lane & 15;
   const int qg = lane >> 4;
   const int wave = wave_id();
-  const int part = blockIdx.x;
   const int T = a.num_query_tokens;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int rows = T * group;  // (query token, query head) rows that read KV head g
   const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
-  const int g = blockIdx.y / wgs;
-  const int row0 = (blockIdx.y % wgs) * (16 * kChunks);
-  const int s = blockIdx.z;
+  const Unit u = unit_of(blockIdx.x, gridDim.x, wgs, a.num_parts, a.num_kv_heads);
+  const int part = u.part;
+  const int g = u.kv_head;
+  const int row0 = u.sibling * (16 * kChunks);
+  const int s = u.seq;
 
   const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
   const int t_lo = part * a.partition_tokens;
@@ -428,25 +466,41 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 // evenly); shorter ones get 4.
 constexpr int kWideTokens = 4096;
 
-// Row chunks per workgroup: every (query token, query head) row of one KV head
-// in one workgroup when there are at most 64, so each K/V tile is read once.
-int chunks_for(int rows) { return rows <= 16 ? 1 : (rows <= 32 ? 2 : 4); }
+// Row chunks per workgroup (at most PA_MAX_CHUNKS; two measured best on
+// MI355X: four chunks hold too much state per lane to keep enough waves
+// resident): the rows of one KV head in as few workgroups as allowed; when they
+// need more, the workgroups become siblings on one XCD.
+#ifndef PA_MAX_CHUNKS
+#define PA_MAX_CHUNKS 2
+#endif
+int chunks_for(int rows) {
+  const int c = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+  return c < PA_MAX_CHUNKS ? c : PA_MAX_CHUNKS;
+}
+
+template <class M, class Tr, int D, int kChunks, bool kShared>
+hipError_t launch_cs(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  // Four chunks hold 64 rows of state per lane: only 4 waves per workgroup fit
+  // them without spilling.
+  if constexpr (kChunks < 4) {
+    if (a.partition_tokens >= kWideTokens) {
+      hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kShared>), grid, dim3(8 * 64), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kShared>), grid, dim3(4 * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
 
 template <class M, class Tr, int D, int kChunks>
 hipError_t launch_c(const DecodeArgs& a, hipStream_t stream) {
   const int rows = a.num_query_tokens * (a.num_q_heads / a.num_kv_heads);
   const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
-  dim3 grid(a.num_parts, a.num_kv_heads * wgs, a.num_seqs);
-  // Four chunks hold 64 rows of state per lane: only 4 waves per workgroup fit
-  // them without spilling.
-  if constexpr (kChunks < 4) {
-    if (a.partition_tokens >= kWideTokens) {
-      hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks>), grid, dim3(8 * 64), 0, stream, a);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks>), grid, dim3(4 * 64), 0, stream, a);
-  return hipGetLastError();
+  const dim3 grid(a.num_parts * a.num_kv_heads * wgs * a.num_seqs);
+  if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true>(a, grid, stream);
+  return launch_cs<M, Tr, D, kChunks, false>(a, grid, stream);
 }
 
 template <class M, class Tr, int D>
@@ -457,8 +511,10 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   } else {
     switch (chunks_for(a.num_query_tokens * (a.num_q_heads / a.num_kv_heads))) {
       case 1: return launch_c<M, Tr, D, 1>(a, stream);
-      case 2: return launch_c<M, Tr, D, 2>(a, stream);
-      default: return launch_c<M, Tr, D, 4>(a, stream);
+#if PA_MAX_CHUNKS >= 4
+      case 4: return launch_c<M, Tr, D, 4>(a, stream);
+#endif
+      default: return launch_c<M, Tr, D, 2>(a, stream);
     }
   }
 }
