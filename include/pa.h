@@ -23,6 +23,7 @@
  *    value and nothing is launched; PA_ERR_HIP reports a failed launch.
  *  - Element dtype: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16), PA_BF16
  *    (bfloat16).  q, out, the pools and new K/V rows share the pool dtype.
+ *    PA_K8_F16 / PA_K8_BF16: int8 keys (see pa_write_kv_k8), 16-bit values.
  *  - KV pool layout.  Both pools are arrays of tiles, one tile per (physical
  *    block, kv head), block-major then head; a tile holds the 16 tokens of the
  *    block, 16 * head_dim elements, contiguous (4 KiB for head_dim 128 in a
@@ -34,7 +35,9 @@
  *      v_pool  [num_blocks][num_kv_heads][head_dim][16]: the tile stores
  *              element 0 of its 16 tokens, then element 1, ...
  *    These orders make every operand of the decode kernel's matrix products a
- *    contiguous per-lane load.
+ *    contiguous per-lane load.  An int8 key pool (PA_K8_*) has the same K
+ *    order with x = 16: [num_blocks][num_kv_heads][head_dim / 16][16][16]
+ *    (2 KiB tiles at head_dim 128); its V pool is the 16-bit one above.
  *  - Block tables: int32 [num_seqs][max_blocks_per_seq], row-major.  Entry j of
  *    row s is the physical block of tokens 16j .. 16j+15 of sequence s.  Only
  *    the first ceil(context_lens[s] / 16) entries of a row are read.
@@ -66,7 +69,16 @@ typedef enum pa_status {
   PA_ERR_NO_SPACE = -6     /* block manager: the pool has too few free + cached blocks */
 } pa_status;
 
-typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  /* Quantised keys: K is int8 with float32 per-(KV head, channel) scales, V,
+   * q and out are 16-bit (f16 or bf16).  Used by pa_write_kv_k8 and
+   * pa_decode_k8; the plain pa_write_kv / pa_decode calls reject them. */
+  PA_K8_F16 = 3,
+  PA_K8_BF16 = 4
+} pa_dtype;
 
 /* Host-side description of a KV pool.  block_size must be 16 and head_dim 64
  * or 128. */
@@ -79,7 +91,8 @@ typedef struct pa_pool_desc {
 } pa_pool_desc;
 
 /* Fill every element of both pools: fill = 0 writes +0.0, fill = 1 writes a
- * quiet NaN (used to prove that unreferenced blocks are never read).  A pool
+ * quiet NaN (used to prove that unreferenced blocks are never read; an int8
+ * key pool gets -128, a code no write produces).  A pool
  * that has just been taken from the allocator (the fixed-capacity block pool of
  * §2.3 of the tanteng.space page). */
 pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int32_t fill,
@@ -175,6 +188,33 @@ pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_
                             int32_t max_context_len, int32_t num_blocks, int64_t* slot_ids,
                             hipStream_t stream);
 
+/* Quantised key cache (§4.2 of the blog.tanteng.space page: keys quantised
+ * per channel, values kept in 16-bit; "KV Cache量化" of the ybb.press page:
+ * INT8 caches, per-channel keys because key channels are unevenly scaled).
+ * The pool dtype is PA_K8_F16 or PA_K8_BF16.  k_scale is float32
+ * [num_kv_heads][head_dim] in device memory: the static scale of each key
+ * channel (e.g. its calibrated max |k| / 127), positive and finite.
+ *
+ * pa_write_kv_k8: as pa_write_kv, but each key element k of channel c becomes
+ *   code = clamp(rint(k / k_scale[g][c]), -127, 127)
+ * (float32 division rounded to nearest, ties to even), stored as int8 in the K
+ * layout above; V rows are copied bit for bit.  k_new and v_new are
+ * [num_tokens][H_kv][d] in the 16-bit type; key rows must be finite.
+ *
+ * pa_decode_k8: pa_verify_decode (num_query_tokens = 1 is pa_decode) over the
+ * dequantised keys code * k_scale[g][c]; q and out in the 16-bit type, split
+ * mode and pa_reduce as there.  A K tile is half the bytes of a 16-bit one:
+ * 3/4 of the KV traffic per token. */
+pa_status pa_write_kv_k8(const pa_pool_desc* pool, void* k_pool, void* v_pool, const float* k_scale,
+                         const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                         int32_t num_tokens, hipStream_t stream);
+pa_status pa_decode_k8(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                       const void* v_pool, const float* k_scale, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_query_tokens, int32_t num_q_heads, int32_t max_context_len,
+                       float scale, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, void* out, hipStream_t stream);
+
 /* Copy whole blocks inside the pool: for each i < num_pairs, block
  * src_dst[2i + 1] of both pools becomes a copy of block src_dst[2i] (every KV
  * head, K and V).  This is the copy of a copy-on-write (§2.3 (2) of the
@@ -190,7 +230,8 @@ pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
  * moves a request's blocks out to host memory and back later).
  * pa_gather_blocks packs blocks block_ids[0 .. n) of both pools contiguously:
  * block i goes to k_dst / v_dst at byte offset i * block_bytes, block_bytes =
- * num_kv_heads * 16 * head_dim * element size (the pool's own tile order).
+ * num_kv_heads * 16 * head_dim * element size of that pool (the pool's own
+ * tile order; 1 byte for int8 keys).
  * pa_scatter_blocks is the inverse: k_src / v_src block i goes to pool block
  * block_ids[i].  block_ids is int32 in device memory; ids outside the pool are
  * skipped.  The packed buffers must be device-accessible (device memory, or

@@ -151,11 +151,65 @@ __global__ __launch_bounds__(256) void write_kv_kernel(char* k_pool, char* v_poo
 }
 
 // ---------------------------------------------------------------------------
+// write_kv_k8: as write_kv, with each key element quantised to int8 by its
+// channel's scale: code = clamp(rint(k / scale), -127, 127), the quotient an
+// IEEE float32 division rounded to nearest and rint rounding ties to even.
+// One thread per 16 channels of one token and KV head: two 16-byte loads of
+// the 16-bit key row, one 16-byte store of codes into the int8 tile
+// ([d / 16][16][16]); the 16 value elements land in 16 columns of the V tile.
+// ---------------------------------------------------------------------------
+template <class Tr, typename E>
+__global__ __launch_bounds__(256) void write_kv_k8_kernel(char* k_pool, char* v_pool,
+                                                          const float* k_scale,
+                                                          const uint4* k_new, const uint4* v_new,
+                                                          const int64_t* slot_mapping,
+                                                          int num_tokens, int64_t num_slots,
+                                                          int num_kv_heads, int head_dim) {
+  const int groups = head_dim / 16;  // 16-channel groups per row
+  const int per_token = num_kv_heads * groups;
+  const int64_t total = static_cast<int64_t>(num_tokens) * per_token;
+  for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int tok = static_cast<int>(idx / per_token);
+    const int64_t slot = slot_mapping[tok];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int rem = static_cast<int>(idx % per_token);
+    const int g = rem / groups;
+    const int cg = rem % groups;
+    const int64_t phys = slot / kBlockSize;
+    const int o = static_cast<int>(slot % kBlockSize);
+    const size_t tile = (static_cast<size_t>(phys) * num_kv_heads + g) * kBlockSize * head_dim;
+    const size_t row = (static_cast<size_t>(tok) * num_kv_heads + g) * head_dim + 16 * cg;  // elements
+    float kf[16];
+    Tr::unpack(k_new[row / 8], kf);
+    Tr::unpack(k_new[row / 8 + 1], kf + 8);
+    const float* sc = k_scale + static_cast<size_t>(g) * head_dim + 16 * cg;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float c = __builtin_rintf(__fdiv_rn(kf[e], sc[e]));
+      c = fminf(fmaxf(c, -127.f), 127.f);
+      const uint32_t b = static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xffu;
+      w[e / 4] |= b << (8 * (e % 4));
+    }
+    *reinterpret_cast<uint4*>(k_pool + tile + (static_cast<size_t>(cg) * kBlockSize + o) * 16) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+    E ve[16];
+    __builtin_memcpy(ve, &v_new[row / 8], 16);
+    __builtin_memcpy(ve + 8, &v_new[row / 8 + 1], 16);
+    E* vt = reinterpret_cast<E*>(v_pool) + tile;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vt[(16 * cg + e) * kBlockSize + o] = ve[e];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // whole-block moves (copy-on-write copies, swap gather / scatter).  Pair p
 // moves block src(p) of the source K and V buffers to block dst(p) of the
 // destination ones, where src(p) = src_ids[p * src_stride] (or p when src_ids
 // is null) and likewise for dst.  A block is block_bytes of contiguous tiles
-// (every KV head).  Pairs with an id outside its buffer's limit are skipped, and
+// (every KV head; K and V blocks may differ in size).  Pairs with an id outside
+// its buffer's limit are skipped, and
 // so are src == dst pairs when skip_equal is set (a copy inside one pool).
 // blockIdx.z selects K (0) or V (1); pairs are strided over blockIdx.y.
 // ---------------------------------------------------------------------------
@@ -164,10 +218,11 @@ __global__ __launch_bounds__(256) void block_move_kernel(const uint4* src_k, con
                                                          const int32_t* src_ids, int src_stride,
                                                          int src_limit, const int32_t* dst_ids,
                                                          int dst_stride, int dst_limit,
-                                                         int num_pairs, size_t block16,
-                                                         bool skip_equal) {
+                                                         int num_pairs, size_t k_block16,
+                                                         size_t v_block16, bool skip_equal) {
   const uint4* src = blockIdx.z == 0 ? src_k : src_v;
   uint4* dst = blockIdx.z == 0 ? dst_k : dst_v;
+  const size_t block16 = blockIdx.z == 0 ? k_block16 : v_block16;
   for (int p = blockIdx.y; p < num_pairs; p += gridDim.y) {
     const int sb = src_ids ? src_ids[static_cast<size_t>(p) * src_stride] : p;
     const int db = dst_ids ? dst_ids[static_cast<size_t>(p) * dst_stride] : p;
@@ -241,8 +296,24 @@ hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const 
   return hipGetLastError();
 }
 
+hipError_t launch_write_kv_k8(void* k_pool, void* v_pool, const float* k_scale, const void* k_new,
+                              const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t dtype, hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 16);
+  auto kernel = dtype == PA_K8_F16 ? write_kv_k8_kernel<F16, uint16_t>
+                                   : write_kv_k8_kernel<BF16, uint16_t>;
+  hipLaunchKernelGGL(kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
+                     static_cast<char*>(k_pool), static_cast<char*>(v_pool), k_scale,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * kBlockSize,
+                     num_kv_heads, head_dim);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream) {
-  const size_t block16 = a.block_bytes / 16;
+  const size_t k16 = a.k_block_bytes / 16, v16 = a.v_block_bytes / 16;
+  const size_t block16 = k16 > v16 ? k16 : v16;
   const int64_t xg = static_cast<int64_t>((block16 + 255) / 256);
   const unsigned gx = static_cast<unsigned>(xg < 1 ? 1 : (xg > 64 ? 64 : xg));
   const unsigned gy = static_cast<unsigned>(a.num_pairs < 1 ? 1 : (a.num_pairs > 65535 ? 65535 : a.num_pairs));
@@ -250,7 +321,7 @@ hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream) {
                      static_cast<const uint4*>(a.src_k), static_cast<const uint4*>(a.src_v),
                      static_cast<uint4*>(a.dst_k), static_cast<uint4*>(a.dst_v), a.src_ids,
                      a.src_stride, a.src_limit, a.dst_ids, a.dst_stride, a.dst_limit, a.num_pairs,
-                     block16, a.skip_equal);
+                     k16, v16, a.skip_equal);
   return hipGetLastError();
 }
 

@@ -110,13 +110,15 @@ __device__ __forceinline__ T load16(const T* p) {
 // element-type specific operand handling
 // ---------------------------------------------------------------------------
 struct MmaBF16 {
-  static constexpr int kBytes = 2;
+  static constexpr int kKBytes = 2;  // bytes per K element
+  static constexpr int kVBytes = 2;  // bytes per V (and q, out) element
+  static constexpr int kQOps = 1;    // q operands per 16-byte K load
   using VLoad = uint2;  // 4 tokens of one V column
   using POp = uint2;    // 4 weights
   // one 16-byte chunk per lane = one 16x16x32 step
-  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4& q, f32x4 c) {
+  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4* q, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
-                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+                                                   __builtin_bit_cast(bf16x8, q[0]), c, 0, 0, 0);
   }
   static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v),
@@ -141,12 +143,14 @@ struct MmaBF16 {
 };
 
 struct MmaF16 {
-  static constexpr int kBytes = 2;
+  static constexpr int kKBytes = 2;
+  static constexpr int kVBytes = 2;
+  static constexpr int kQOps = 1;
   using VLoad = uint2;
   using POp = uint2;
-  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4& q, f32x4 c) {
+  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4* q, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
-                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
+                                                  __builtin_bit_cast(f16x8, q[0]), c, 0, 0, 0);
   }
   static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
@@ -163,14 +167,17 @@ struct MmaF16 {
 };
 
 struct MmaF32 {
-  static constexpr int kBytes = 4;
+  static constexpr int kKBytes = 4;
+  static constexpr int kVBytes = 4;
+  static constexpr int kQOps = 1;
   using VLoad = uint4;  // 4 tokens of one V column
   struct POp {
     float p[4];
   };
   // a 16-byte chunk holds 4 elements: four 16x16x4 steps, element e of every
   // lane's chunk forming step e
-  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4& q, f32x4 c) {
+  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4* qp, f32x4 c) {
+    const uint4 q = qp[0];
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.x), __uint_as_float(q.x), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.y), __uint_as_float(q.y), c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.z), __uint_as_float(q.z), c, 0, 0, 0);
@@ -195,6 +202,48 @@ struct MmaF32 {
     if (n < 3) v.z = 0u;
     if (n < 4) v.w = 0u;
   }
+};
+
+// Int8 keys with float32 per-channel scales; values (and q, out) of the 16-bit
+// type of VM.  A 16-byte K load brings 16 channels of one token: two 16x16x32
+// f16 steps, the low 8 channels against q operand 0 and the high 8 against
+// operand 1.  The B operand is q' = q * scale per channel (times a power of
+// two per row, taken out again on the logits), rounded to f16; the codes
+// convert to f16 exactly, so the matrix cores see exact integers.
+template <class VM>
+struct MmaK8 {
+  static constexpr int kKBytes = 1;
+  static constexpr int kVBytes = 2;
+  static constexpr int kQOps = 2;
+  using VLoad = typename VM::VLoad;
+  using POp = typename VM::POp;
+  // 8 int8 codes (two words) -> f16x8.  code ^ 0x80 is the offset-binary byte
+  // u = code + 128; the f16 with bits 0x6400 | u is 1024 + u, so subtracting
+  // 1152 leaves the code (all integers below 2048 are exact in f16).
+  static __device__ __forceinline__ f16x8 codes(uint32_t w0, uint32_t w1) {
+    w0 ^= 0x80808080u;
+    w1 ^= 0x80808080u;
+    constexpr uint32_t kExp = 0x64646464u;
+    const u32x4 h = {__builtin_amdgcn_perm(kExp, w0, 0x04010400u),
+                     __builtin_amdgcn_perm(kExp, w0, 0x04030402u),
+                     __builtin_amdgcn_perm(kExp, w1, 0x04010400u),
+                     __builtin_amdgcn_perm(kExp, w1, 0x04030402u)};
+    return __builtin_bit_cast(f16x8, h) - static_cast<_Float16>(1152.0f);
+  }
+  static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4* q, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes(k.x, k.y), __builtin_bit_cast(f16x8, q[0]), c,
+                                               0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes(k.z, k.w), __builtin_bit_cast(f16x8, q[1]), c,
+                                               0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
+    return VM::pv(v, p, c);
+  }
+  static __device__ __forceinline__ POp pack(const float (&p)[4], float& sum) {
+    return VM::pack(p, sum);
+  }
+  static __device__ __forceinline__ void keep(VLoad& v, int n) { VM::keep(v, n); }
 };
 
 // maximum / sum over the four lanes r, r+16, r+32, r+48 (lane-swap butterflies)
@@ -254,7 +303,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   // another, so their loads must not carry the streaming hint.
   constexpr bool kStreamK = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 2);
   constexpr bool kStreamV = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 3);
-  constexpr int kKLoads = D * M::kBytes / 64;  // 1 KiB K loads per tile (= 16-byte chunks / 4)
+  constexpr int kKLoads = D * M::kKBytes / 64;  // 1 KiB K loads per tile (= 16-byte chunks / 4)
+  constexpr int kQOps = kKLoads * M::kQOps;      // B operands of the logits per row
   constexpr int kColBlocks = D / 16;           // P.V output blocks of 16 columns
   constexpr int kPad = 4;                      // LDS row padding (floats)
   using VLoad = typename M::VLoad;
@@ -287,11 +337,12 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   // limit of this workgroup's rows are masked row by row.
   const int t_hi_min = min(t_hi, L - T + 1 + row0 / group);
 
-  // Per chunk c, lane l holds row row0 + 16 c + r: the B operand of its logits
-  // (chunk 4j + qg of that row's query vector, zero for padding rows), its token
-  // limit, and its online-softmax state.
-  uint4 qop[kChunks][kKLoads];
+  // Per chunk c, lane l holds row row0 + 16 c + r: the B operands of its logits
+  // (for 16-bit keys chunk 4j + qg of that row's query vector; zero for padding
+  // rows), its token limit, the scale of its logits and its online-softmax state.
+  uint4 qop[kChunks][kQOps];
   int row_hi[kChunks];
+  float qs[kChunks];  // logits in log2 units: scale * log2(e) (and the K8 row factor)
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int rho = row0 + 16 * c + r;
@@ -300,15 +351,60 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     const int i = rr / group;
     const int hq = g * group + rr % group;
     const char* qrow = static_cast<const char*>(a.q) +
-                       ((static_cast<size_t>(s) * T + i) * a.num_q_heads + hq) * D * M::kBytes;
+                       ((static_cast<size_t>(s) * T + i) * a.num_q_heads + hq) * D * M::kVBytes;
+    qs[c] = a.scale * kLog2e;
+    if constexpr (M::kQOps == 1) {
 #pragma unroll
-    for (int j = 0; j < kKLoads; ++j) {
-      const uint4 v = reinterpret_cast<const uint4*>(qrow)[4 * j + qg];
-      qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < kKLoads; ++j) {
+        const uint4 v = reinterpret_cast<const uint4*>(qrow)[4 * j + qg];
+        qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+      // int8 keys: load j brings channels 16 (4j + qg) .. + 15 of a token; the
+      // matching q' = q * k_scale, scaled by 2^e so that the row's largest
+      // |q'| lies in [2^13, 2^14) (full f16 precision whatever the scales),
+      // and 2^-e folded into the logit scale.
+      const float* ks = a.k_scale + static_cast<size_t>(g) * D;
+      float qp[kKLoads][16];
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < kKLoads; ++j) {
+        const int ch = 16 * (4 * j + qg);
+        float e[16];
+        Tr::unpack(reinterpret_cast<const uint4*>(qrow)[ch / 8], e);
+        Tr::unpack(reinterpret_cast<const uint4*>(qrow)[ch / 8 + 1], e + 8);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float4 sc4 = reinterpret_cast<const float4*>(ks + ch)[t];
+          qp[j][4 * t + 0] = e[4 * t + 0] * sc4.x;
+          qp[j][4 * t + 1] = e[4 * t + 1] * sc4.y;
+          qp[j][4 * t + 2] = e[4 * t + 2] * sc4.z;
+          qp[j][4 * t + 3] = e[4 * t + 3] * sc4.w;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fabsf(qp[j][t]));
+      }
+      mx = max_over_q(mx);  // the row's four lanes
+      int ex = 0;
+      if (mx > 0.f) {
+        (void)frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+      }
+      const float up = ldexpf(1.f, 14 - ex);
+      qs[c] *= ldexpf(1.f, ex - 14);
+#pragma unroll
+      for (int j = 0; j < kKLoads; ++j) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          f16x8 h;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) h[t] = static_cast<_Float16>(qp[j][8 * hh + t] * up);
+          const uint4 v = __builtin_bit_cast(uint4, h);
+          qop[c][2 * j + hh] = live ? v : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
     }
     row_hi[c] = live ? min(t_hi, L - T + 1 + i) : t_hi;
   }
-  const float qs = a.scale * kLog2e;  // logits in log2 units
 
   float m[kChunks];     // running maximum (log2 units) of row r, shared by its 4 lanes
   float lsum[kChunks];  // this lane's share of the running sum
@@ -329,9 +425,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   auto physical = [&](int jb) { return pa_physical_block(trow, jb, a.num_blocks); };
 
   auto load = [&](int phys, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
-    const size_t tile = pa_tile_offset(phys, g, a.num_kv_heads, D) * M::kBytes;
-    const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile);
-    const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + tile);
+    const size_t tile = pa_tile_offset(phys, g, a.num_kv_heads, D);  // elements
+    const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile * M::kKBytes);
+    const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + tile * M::kVBytes);
 #pragma unroll
     for (int j = 0; j < kKLoads; ++j) kr[j] = load16<kStreamK>(kt + 64 * j + lane);
 #pragma unroll
@@ -350,10 +446,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     for (int c = 0; c < kChunks; ++c) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < kKLoads; ++j) sc = M::qk(kr[j], qop[c][j], sc);
+      for (int j = 0; j < kKLoads; ++j) sc = M::qk(kr[j], &qop[c][j * M::kQOps], sc);
       float x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs;
+      for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs[c];
       if (masked) {
         const int n = min(max(row_hi[c] - tok0, 0), 4);
 #pragma unroll
@@ -505,7 +601,7 @@ hipError_t launch_c(const DecodeArgs& a, hipStream_t stream) {
 
 template <class M, class Tr, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  if constexpr (M::kBytes == 4 && D == 128) {
+  if constexpr (M::kKBytes == 4 && D == 128) {
     // an 8 KiB float32 tile fills the registers already: one chunk per workgroup
     return launch_c<M, Tr, D, 1>(a, stream);
   } else {
@@ -530,6 +626,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.dtype) {
     case PA_F32: return launch_dim<MmaF32, F32>(a, stream);
     case PA_F16: return launch_dim<MmaF16, F16>(a, stream);
+    case PA_K8_F16: return launch_dim<MmaK8<MmaF16>, F16>(a, stream);
+    case PA_K8_BF16: return launch_dim<MmaK8<MmaBF16>, BF16>(a, stream);
     default: return launch_dim<MmaBF16, BF16>(a, stream);
   }
 }

@@ -15,6 +15,7 @@ struct DecodeArgs {
   const void* q;
   const void* k_pool;
   const void* v_pool;
+  const float* k_scale;  // int8 keys: float32 [H_kv][d] channel scales; else null
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t max_blocks_per_seq;
@@ -72,10 +73,16 @@ struct BlockMoveArgs {
   int32_t dst_stride;
   int32_t dst_limit;
   int32_t num_pairs;
-  size_t block_bytes;      // a multiple of 16
+  size_t k_block_bytes;    // bytes of one block of the K buffers (a multiple of 16)
+  size_t v_block_bytes;    // bytes of one block of the V buffers (a multiple of 16)
   bool skip_equal;
 };
 hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream);
+
+hipError_t launch_write_kv_k8(void* k_pool, void* v_pool, const float* k_scale, const void* k_new,
+                              const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t dtype, hipStream_t stream);
 
 hipError_t launch_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,

@@ -23,14 +23,14 @@ PA_ERR_WORKSPACE = -4
 PA_ERR_HIP = -5
 PA_ERR_NO_SPACE = -6
 
-PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_F32, PA_F16, PA_BF16, PA_K8_F16, PA_K8_BF16 = 0, 1, 2, 3, 4
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 NAME_TO_PA = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_init_pool", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
-           "pa_verify_decode", "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
+           "pa_verify_decode", "pa_write_kv_k8", "pa_decode_k8", "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
            "pa_scatter_blocks", "pa_status_string")
 
 
@@ -75,6 +75,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_verify_decode.restype = ctypes.c_int
     lib.pa_verify_decode.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                      ctypes.c_float, i32, vp, sz, vp, vp]
+    lib.pa_write_kv_k8.restype = ctypes.c_int
+    lib.pa_write_kv_k8.argtypes = [desc, vp, vp, vp, vp, vp, i64p, i32, vp]
+    lib.pa_decode_k8.restype = ctypes.c_int
+    lib.pa_decode_k8.argtypes = [desc, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                 ctypes.c_float, i32, vp, sz, vp, vp]
     lib.pa_reduce.restype = ctypes.c_int
     lib.pa_reduce.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_debug_slot_ids.restype = ctypes.c_int
@@ -111,10 +116,16 @@ def _check(fn: str, status: int) -> None:
         raise PAError(fn, status)
 
 
-def pool_desc(k_pool: torch.Tensor) -> PoolDesc:
-    """Descriptor of a K pool tensor shaped [num_blocks][H_kv][d / x][16][x]."""
+def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor | None = None) -> PoolDesc:
+    """Descriptor of a K pool tensor shaped [num_blocks][H_kv][d / x][16][x].  An
+    int8 K pool (quantised keys) takes its value type from ``v_pool``."""
     nb, hkv, nchunk, bs, x = k_pool.shape
-    return PoolDesc(nb, bs, hkv, nchunk * x, TORCH_TO_PA.get(k_pool.dtype, -1))
+    if k_pool.dtype == torch.int8:
+        vt = None if v_pool is None else v_pool.dtype
+        dt = {torch.float16: PA_K8_F16, torch.bfloat16: PA_K8_BF16}.get(vt, -1)
+    else:
+        dt = TORCH_TO_PA.get(k_pool.dtype, -1)
+    return PoolDesc(nb, bs, hkv, nchunk * x, dt)
 
 
 def pa_status_string(status: int) -> str:
@@ -122,13 +133,13 @@ def pa_status_string(status: int) -> str:
 
 
 def pa_init_pool(k_pool, v_pool, fill: int = 0, stream=None) -> None:
-    desc = pool_desc(k_pool)
+    desc = pool_desc(k_pool, v_pool)
     _check("pa_init_pool", load().pa_init_pool(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
                                                fill, _stream(stream)))
 
 
 def pa_write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
-    desc = pool_desc(k_pool)
+    desc = pool_desc(k_pool, v_pool)
     n = int(slot_mapping.shape[0])
     _check("pa_write_kv", load().pa_write_kv(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
                                              _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n,
@@ -143,7 +154,7 @@ def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
 
 def pa_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int, scale: float,
               partition_size: int = 0, workspace=None, out=None, stream=None) -> None:
-    desc = pool_desc(k_pool)
+    desc = pool_desc(k_pool, v_pool)
     B, Hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_decode", load().pa_decode(
@@ -156,11 +167,33 @@ def pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_
                      scale: float, partition_size: int = 0, workspace=None, out=None,
                      stream=None) -> None:
     """q and out: [B][T][H_q][d] (T draft tokens per sequence)."""
-    desc = pool_desc(k_pool)
+    desc = pool_desc(k_pool, v_pool)
     B, T, Hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pa_verify_decode", load().pa_verify_decode(
         ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq, int(max_context_len),
+        float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
+
+
+def pa_write_kv_k8(k_pool, v_pool, k_scale, k_new, v_new, slot_mapping, stream=None) -> None:
+    """int8 key pool: k_new / v_new [T][H_kv][d] in the value type, k_scale float32 [H_kv][d]."""
+    desc = pool_desc(k_pool, v_pool)
+    n = int(slot_mapping.shape[0])
+    _check("pa_write_kv_k8", load().pa_write_kv_k8(
+        ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(k_new), _ptr(v_new),
+        _ptr(slot_mapping), n, _stream(stream)))
+
+
+def pa_decode_k8(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_context_len: int,
+                 scale: float, partition_size: int = 0, workspace=None, out=None,
+                 stream=None) -> None:
+    """q and out: [B][T][H_q][d] in the value type (T = 1: decode)."""
+    desc = pool_desc(k_pool, v_pool)
+    B, T, Hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pa_decode_k8", load().pa_decode_k8(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq, int(max_context_len),
         float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
 
@@ -183,21 +216,21 @@ def pa_debug_slot_ids(block_tables, context_lens, max_context_len: int, num_bloc
 
 def pa_copy_blocks(k_pool, v_pool, src_dst, stream=None) -> None:
     """src_dst: int32 device tensor [n][2] of (source, destination) blocks."""
-    desc = pool_desc(k_pool)
+    desc = pool_desc(k_pool, v_pool)
     n = int(src_dst.shape[0]) if src_dst is not None else 0
     _check("pa_copy_blocks", load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
                                                    _ptr(src_dst), n, _stream(stream)))
 
 
 def pa_gather_blocks(k_pool, v_pool, block_ids, k_dst, v_dst, stream=None) -> None:
-    desc = pool_desc(k_pool)
+    desc = pool_desc(k_pool, v_pool)
     _check("pa_gather_blocks", load().pa_gather_blocks(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
         _ptr(k_dst), _ptr(v_dst), _stream(stream)))
 
 
 def pa_scatter_blocks(k_pool, v_pool, block_ids, k_src, v_src, stream=None) -> None:
-    desc = pool_desc(k_pool)
+    desc = pool_desc(k_pool, v_pool)
     _check("pa_scatter_blocks", load().pa_scatter_blocks(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
         _ptr(k_src), _ptr(v_src), _stream(stream)))
@@ -251,4 +284,25 @@ def verify_attention(q, k_pool, v_pool, block_tables, context_lens, max_context_
     else:
         pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale, 0,
                          None, out, stream)
+    return out
+
+
+def k8_attention(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_context_len: int,
+                 scale: float, partition_size: int = 0, workspace=None, out=None, stream=None):
+    """out = pa_decode_k8 (+ pa_reduce over T * H_q rows when split).  q is
+    [B][T][H_q][d]; returns out of the same shape."""
+    if out is None:
+        out = torch.empty_like(q)
+    B, T, Hq, D = q.shape
+    if partition_size > 0:
+        if workspace is None:
+            n = pa_decode_workspace_bytes(B, T * Hq, D, max_context_len, partition_size)
+            workspace = torch.empty(n // 4, dtype=torch.float32, device=q.device)
+        pa_decode_k8(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_context_len, scale,
+                     partition_size, workspace, None, stream)
+        pa_reduce(workspace, context_lens, B, T * Hq, D, max_context_len, partition_size, out,
+                  stream)
+    else:
+        pa_decode_k8(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_context_len, scale,
+                     0, None, out, stream)
     return out

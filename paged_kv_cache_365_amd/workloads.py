@@ -153,9 +153,13 @@ class Workload:
     def group(self) -> int:
         return self.num_q_heads // self.num_kv_heads
 
-    def kv_bytes_logical(self) -> int:
-        """K+V bytes one decode call reads, counting shared blocks once per reference."""
-        per_token = 2 * self.num_kv_heads * self.head_dim * ELEM_BYTES[self.dtype]
+    def kv_bytes_logical(self, key_bytes: int | None = None) -> int:
+        """K+V bytes one decode call reads, counting shared blocks once per reference
+        (``key_bytes``: bytes per key element when keys are stored narrower than
+        values, e.g. 1 for int8 keys)."""
+        e = ELEM_BYTES[self.dtype]
+        kb = e if key_bytes is None else key_bytes
+        per_token = self.num_kv_heads * self.head_dim * (kb + e)
         return int(self.context_lens.astype(np.int64).sum()) * per_token
 
     def kv_bytes_unique(self) -> int:
@@ -167,15 +171,56 @@ class Workload:
             return int(shared + (lens - shared).sum()) * per_token
         return int(lens.sum()) * per_token
 
-    def algorithmic_bytes(self, unique: bool = False, query_tokens: int = 1) -> int:
+    def algorithmic_bytes(self, unique: bool = False, query_tokens: int = 1,
+                          key_bytes: int | None = None) -> int:
         """KV + q + out + live block-table entries + context_lens (q and out hold
         ``query_tokens`` rows per sequence and head: 1 for decode, T for a verify
-        call over a T-token draft)."""
+        call over a T-token draft).  With int8 keys (``key_bytes`` = 1) the
+        float32 channel scales are read too."""
         e = ELEM_BYTES[self.dtype]
         qo = 2 * query_tokens * self.num_seqs * self.num_q_heads * self.head_dim * e
         live_entries = int(((self.context_lens.astype(np.int64) + BLOCK_SIZE - 1) // BLOCK_SIZE).sum())
-        kv = self.kv_bytes_unique() if unique else self.kv_bytes_logical()
-        return kv + qo + 4 * live_entries + 4 * self.num_seqs
+        if unique:
+            kv = self.kv_bytes_unique()
+        else:
+            kv = self.kv_bytes_logical(key_bytes)
+        scales = 4 * self.num_kv_heads * self.head_dim if key_bytes == 1 else 0
+        return kv + qo + 4 * live_entries + 4 * self.num_seqs + scales
+
+
+# --------------------------------------------------------------------------
+# quantised keys: an int8 key cache over a workload's tables
+# --------------------------------------------------------------------------
+K8_POISON = -128           # a code no quantised write produces: marks unwritten slots
+K8_CODE_SPREAD = 30.0      # codes ~ N(0, 30^2): N(0,1) keys at scale 4.2 / 127
+K8_BASE_SCALE = 4.2 / 127.0
+
+
+def k8_inputs(w: "Workload", seed: int, outlier_columns: int = 0, outlier_gain: float = 10.0):
+    """An int8 key cache for ``w``'s pool, tables and shapes (``w``'s V pool, q
+    and tables are used with it): codes [NB][H_kv][d/16][16][16] drawn as integers
+    near N(0, 30^2) (rounded draws, clamped to +-127), and float32 channel scales
+    [H_kv][d] of 4.2/127, times ``outlier_gain`` on ``outlier_columns`` random
+    (KV head, channel) columns -- the per-channel key outliers.  Free blocks and
+    the slots past each context in its last block hold -128.  Returns
+    (k8_pool int8, k_scale float32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    NB, Hkv, d = w.num_blocks, w.num_kv_heads, w.head_dim
+    shape = (NB, Hkv, d // 16, BLOCK_SIZE, 16)
+    draws = normal(rng, shape, "f32", gain=K8_CODE_SPREAD)
+    codes = np.clip(np.rint(draws), -127, 127).astype(np.int8)
+    k_scale = np.full((Hkv, d), K8_BASE_SCALE, dtype=np.float32)
+    if outlier_columns:
+        cols = rng.choice(Hkv * d, size=outlier_columns, replace=False)
+        k_scale.reshape(-1)[cols] *= np.float32(outlier_gain)
+    if w.free_blocks is not None and len(w.free_blocks):
+        codes[w.free_blocks] = K8_POISON
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        o = L % BLOCK_SIZE
+        if L and o:
+            codes[w.block_tables[s, L // BLOCK_SIZE], :, :, o:, :] = K8_POISON
+    return codes, k_scale
 
 
 def _scale_for(head_dim: int) -> float:

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "pa.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -149,3 +149,28 @@ def test_verify_rejects_bad_arguments(lib):
     # split mode needs room for T * H_q rows per sequence
     need = pa.pa_decode_workspace_bytes(2, 4 * 4, 64, 40, 16)
     assert call(P=16, ws=FAKE, ws_bytes=need - 4) == pa.PA_ERR_WORKSPACE
+
+
+def test_k8_calls_reject_bad_arguments(lib):
+    k8 = _desc(dtype=pa.PA_K8_BF16)
+    plain = _desc(dtype=pa.PA_BF16)
+    w8 = lib.pa_write_kv_k8
+    assert w8(ctypes.byref(k8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == pa.PA_OK
+    assert w8(ctypes.byref(plain), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    assert w8(ctypes.byref(k8), FAKE, FAKE, None, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_INVALID_ARG
+    assert w8(ctypes.byref(k8), FAKE, FAKE, FAKE + 2, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_MISALIGNED
+    # the plain calls refuse an int8 key pool: its keys need their scales
+    assert lib.pa_write_kv(ctypes.byref(k8), FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    assert _decode(lib, desc=k8) == pa.PA_ERR_UNSUPPORTED
+    d8 = lib.pa_decode_k8
+
+    def call(desc=k8, ks=FAKE, T=1, q=FAKE):
+        return d8(ctypes.byref(desc), q, FAKE, FAKE, ks, FAKE, 4, FAKE, 2, T, 4, 40, 0.125, 0,
+                  None, 0, FAKE, None)
+    assert call(ks=None) == pa.PA_ERR_INVALID_ARG
+    assert call(desc=plain) == pa.PA_ERR_UNSUPPORTED
+    assert call(ks=FAKE + 4) == pa.PA_ERR_MISALIGNED      # the kernel reads scales 16 bytes at a time
+    assert call(T=0) == pa.PA_ERR_INVALID_ARG
+    # pa_reduce writes a plain 16-bit output
+    assert lib.pa_reduce(FAKE, FAKE, 2, 4, 64, 40, 16, pa.PA_K8_BF16, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert pa.pa_status_string(pa.PA_OK) == "PA_OK"
