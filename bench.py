@@ -143,6 +143,9 @@ def main() -> int:
     ap.add_argument("--tuned", action="store_true",
                     help="use the tuned partition size even where the workload names its own")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--longest-first", action="store_true",
+                    help="order the batch by context length, longest first, as a scheduler "
+                         "would with pa_bm_sort_longest_first (the workload is otherwise as drawn)")
     ap.add_argument("--kv", choices=("native", "k8"), default="native",
                     help="k8: int8 keys with per-channel scales (pa_decode_k8), values in the "
                          "workload's 16-bit type")
@@ -174,6 +177,11 @@ def main() -> int:
 
     log(f"generating workload {args.config}")
     w = wl.make_config(args.config, args.seed)
+    if args.longest_first:
+        import dataclasses
+        order = np.argsort(-w.context_lens.astype(np.int64), kind="stable")
+        w = dataclasses.replace(w, q=w.q[order], block_tables=w.block_tables[order],
+                                context_lens=w.context_lens[order])
     P = tuning.partition_for(w, own=not args.tuned) if args.partition is None else args.partition
     d = upload(w, "cuda")
     T = max(args.verify, 1)
@@ -294,7 +302,8 @@ def main() -> int:
         "config": {
             "workload": workload, "num_seqs": B, "query_tokens": T, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
             "head_dim": D, "max_context_len": w.max_context_len, "block_size": 16,
-            "partition_size": P, "pool_blocks": w.num_blocks, "seed": args.seed if args.seed is not None else 1000 + args.config,
+            "partition_size": P, "pool_blocks": w.num_blocks,
+            "batch_order": "longest-first" if args.longest_first else "as drawn", "seed": args.seed if args.seed is not None else 1000 + args.config,
         },
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),

@@ -133,6 +133,16 @@ pa_status pa_bm_get_table(const pa_block_manager* bm, int64_t seq_id, int32_t* r
 pa_status pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                             int32_t* tables, int32_t max_blocks_per_seq, int32_t* context_lens);
 
+/* A decode batch in dispatch-friendly order: out_ids = seq_ids sorted by
+ * context length, longest first (equal lengths keep their input order).  The
+ * decode kernel hands out its work in batch order, so a ragged batch whose
+ * long sequences come first finishes its tail with short ones (measured on
+ * MI355X, 32 sequences of U[512, 4096] tokens: 201.5 us in drawn order, 174.4
+ * us longest first).  The caller builds q and reads out in this order.
+ * out_ids may alias seq_ids. */
+pa_status pa_bm_sort_longest_first(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                                   int64_t* out_ids);
+
 pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* stats);
 
 /* Reference count of a physical block (-1 when out of range). */

@@ -237,3 +237,9 @@ def append_step(model: BlockManagerModel, seqs, token_ids=None):
         if cp is not None:
             copies.append(cp)
     return slots, copies
+
+
+def sort_longest_first(model: BlockManagerModel, seqs):
+    """The batch ordered by context length, longest first; equal lengths keep
+    their order."""
+    return sorted(seqs, key=lambda s: -model.lens[s])

@@ -17,7 +17,8 @@ from . import pa
 EXPORTS = ("pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_match_prefix",
            "pa_bm_append", "pa_bm_append_step", "pa_bm_fork", "pa_bm_free_seq",
            "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_get_table", "pa_bm_fill_tables",
-           "pa_bm_get_stats", "pa_bm_refcount", "pa_bm_blocks_needed")
+           "pa_bm_get_stats", "pa_bm_refcount", "pa_bm_blocks_needed",
+           "pa_bm_sort_longest_first")
 
 
 class Stats(ctypes.Structure):
@@ -54,6 +55,7 @@ def _lib():
             "pa_bm_get_stats": [vp, vp],
             "pa_bm_refcount": [vp, i32],
             "pa_bm_blocks_needed": [vp, i64, i32],
+            "pa_bm_sort_longest_first": [vp, vp, i32, vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -172,6 +174,14 @@ class BlockManager:
         pa._check("pa_bm_fill_tables", self._lib.pa_bm_fill_tables(
             self._h, _p(ids), n, _p(tables), int(max_blocks_per_seq), _p(lens)))
         return tables[:n], lens[:n]
+
+    def sort_longest_first(self, seqs):
+        """The batch ``seqs`` ordered by context length, longest first (stable)."""
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        out = np.empty(max(ids.size, 1), dtype=np.int64)
+        pa._check("pa_bm_sort_longest_first", self._lib.pa_bm_sort_longest_first(
+            self._h, _p(ids), int(ids.size), _p(out)))
+        return out[: ids.size]
 
     def stats(self) -> dict:
         st = Stats()

@@ -12,6 +12,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -377,6 +378,23 @@ pa_status pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, 
     for (int32_t j = nb; j < max_blocks_per_seq; ++j) row[j] = -1;
     context_lens[i] = ss[i]->len;
   }
+  return PA_OK;
+}
+
+pa_status pa_bm_sort_longest_first(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                                   int64_t* out_ids) {
+  if (!valid_bm(bm) || n < 0 || (n > 0 && (!seq_ids || !out_ids))) return PA_ERR_INVALID_ARG;
+  std::vector<std::pair<int32_t, int64_t>> v(static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PA_ERR_INVALID_ARG;
+    v[i] = {it->second.len, seq_ids[i]};
+  }
+  std::stable_sort(v.begin(), v.end(),
+                   [](const std::pair<int32_t, int64_t>& x, const std::pair<int32_t, int64_t>& y) {
+                     return x.first > y.first;
+                   });
+  for (int32_t i = 0; i < n; ++i) out_ids[i] = v[i].second;
   return PA_OK;
 }
 

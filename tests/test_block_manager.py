@@ -21,7 +21,8 @@ import random
 import numpy as np
 import pytest
 
-from oracle.block_manager import BLOCK_SIZE, BlockManagerModel, PoolExhausted, append_step
+from oracle.block_manager import (BLOCK_SIZE, BlockManagerModel, PoolExhausted, append_step,
+                                  sort_longest_first)
 from paged_kv_cache_365_amd import pa
 from paged_kv_cache_365_amd.block_manager import EXPORTS, BlockManager
 
@@ -414,6 +415,9 @@ def run_trace(seed, num_blocks, n_ops, impls, vocab=3):
             a, b = impls
             assert a.ref == b.refs()
             assert a.stats() == b.stats()
+            if live:
+                batch = rnd.sample(live, len(live))
+                assert sort_longest_first(a, batch) == b.bm.sort_longest_first(batch).tolist()
     return next_id
 
 
@@ -465,3 +469,18 @@ def test_block_manager_exports():
     assert names == set(EXPORTS)
     for n in names:
         assert hasattr(lib, n)
+
+
+def test_sort_longest_first():
+    m = BlockManagerModel(64)
+    bm = BlockManager(64)
+    for s, n in enumerate([5, 40, 17, 40, 1, 33]):
+        for impl in (m, bm):
+            impl.add_seq(s, False)
+            impl.append(s, n)
+    batch = [4, 3, 0, 1, 5, 2]
+    want = [3, 1, 5, 2, 0, 4]          # lengths 40, 40, 33, 17, 5, 1; ties keep order
+    assert sort_longest_first(m, batch) == want
+    assert bm.sort_longest_first(batch).tolist() == want
+    with pytest.raises(pa.PAError):
+        bm.sort_longest_first([0, 99])
