@@ -143,6 +143,9 @@ def main() -> int:
     ap.add_argument("--tuned", action="store_true",
                     help="use the tuned partition size even where the workload names its own")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--block-size", type=int, default=16, choices=(16, 8),
+                    help="tokens per physical block (8: the smaller blocks the pages mention "
+                         "for 70B models)")
     ap.add_argument("--longest-first", action="store_true",
                     help="order the batch by context length, longest first, as a scheduler "
                          "would with pa_bm_sort_longest_first (the workload is otherwise as drawn)")
@@ -176,7 +179,7 @@ def main() -> int:
     pa.load()
 
     log(f"generating workload {args.config}")
-    w = wl.make_config(args.config, args.seed)
+    w = wl.make_config(args.config, args.seed, block_size=args.block_size)
     if args.longest_first:
         import dataclasses
         order = np.argsort(-w.context_lens.astype(np.int64), kind="stable")
@@ -301,7 +304,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": workload, "num_seqs": B, "query_tokens": T, "num_q_heads": Hq, "num_kv_heads": w.num_kv_heads,
-            "head_dim": D, "max_context_len": w.max_context_len, "block_size": 16,
+            "head_dim": D, "max_context_len": w.max_context_len, "block_size": w.block_size,
             "partition_size": P, "pool_blocks": w.num_blocks,
             "batch_order": "longest-first" if args.longest_first else "as drawn", "seed": args.seed if args.seed is not None else 1000 + args.config,
         },

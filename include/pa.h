@@ -25,22 +25,23 @@
  *    (bfloat16).  q, out, the pools and new K/V rows share the pool dtype.
  *    PA_K8_F16 / PA_K8_BF16: int8 keys (see pa_write_kv_k8), 16-bit values.
  *  - KV pool layout.  Both pools are arrays of tiles, one tile per (physical
- *    block, kv head), block-major then head; a tile holds the 16 tokens of the
- *    block, 16 * head_dim elements, contiguous (4 KiB for head_dim 128 in a
- *    16-bit dtype).  Token slot = physical_block * 16 + offset.  Inside a tile:
- *      k_pool  [num_blocks][num_kv_heads][head_dim / x][16][x], x = 16 bytes /
+ *    block, kv head), block-major then head; a tile holds the bs tokens of the
+ *    block (bs = block_size, 16 or 8), bs * head_dim elements, contiguous (4 KiB
+ *    for 16 tokens at head_dim 128 in a 16-bit dtype).  Token slot =
+ *    physical_block * bs + offset.  Inside a tile:
+ *      k_pool  [num_blocks][num_kv_heads][head_dim / x][bs][x], x = 16 bytes /
  *              element size (8 for f16/bf16, 4 for f32): each token row is cut
- *              into 16-byte chunks and the tile stores chunk 0 of its 16 tokens,
+ *              into 16-byte chunks and the tile stores chunk 0 of its bs tokens,
  *              then chunk 1, ...;
- *      v_pool  [num_blocks][num_kv_heads][head_dim][16]: the tile stores
- *              element 0 of its 16 tokens, then element 1, ...
+ *      v_pool  [num_blocks][num_kv_heads][head_dim][bs]: the tile stores
+ *              element 0 of its bs tokens, then element 1, ...
  *    These orders make every operand of the decode kernel's matrix products a
  *    contiguous per-lane load.  An int8 key pool (PA_K8_*) has the same K
  *    order with x = 16: [num_blocks][num_kv_heads][head_dim / 16][16][16]
- *    (2 KiB tiles at head_dim 128); its V pool is the 16-bit one above.
+ *    (2 KiB tiles of 16 tokens at head_dim 128); its V pool is the 16-bit one.
  *  - Block tables: int32 [num_seqs][max_blocks_per_seq], row-major.  Entry j of
- *    row s is the physical block of tokens 16j .. 16j+15 of sequence s.  Only
- *    the first ceil(context_lens[s] / 16) entries of a row are read.
+ *    row s is the physical block of tokens bs*j .. bs*j + bs-1 of sequence s.
+ *    Only the first ceil(context_lens[s] / bs) entries of a row are read.
  *  - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads)
  *    (contiguous groups; num_q_heads == num_kv_heads is MHA, num_kv_heads == 1 MQA).
  *  - Device-side data are not validated (that would need a synchronisation):
@@ -80,8 +81,9 @@ typedef enum pa_dtype {
   PA_K8_BF16 = 4
 } pa_dtype;
 
-/* Host-side description of a KV pool.  block_size must be 16 and head_dim 64
- * or 128. */
+/* Host-side description of a KV pool.  block_size is 16 (the pages' default)
+ * or 8 (the smaller blocks §2.2 of the blog.tanteng.space page mentions for
+ * 70B models); head_dim is 64 or 128. */
 typedef struct pa_pool_desc {
   int32_t num_blocks;
   int32_t block_size;
@@ -100,9 +102,9 @@ pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int
 
 /* KV append: for each of num_tokens new tokens i, copy k_new[i] and v_new[i]
  * ([num_kv_heads][head_dim] each, pool dtype, so k_new is [num_tokens][H_kv][d])
- * bit for bit into slot slot_mapping[i] = physical * 16 + offset of both pools,
+ * bit for bit into slot slot_mapping[i] = physical * bs + offset of both pools,
  * in the tile layouts above.
- * A negative slot skips the token; slots >= num_blocks * 16 are also skipped.
+ * A negative slot skips the token; slots >= num_blocks * bs are also skipped.
  * Two tokens with the same slot race (the caller's contract).  This is the step
  * that puts the new token's K/V into the cache before attention, as the
  * KVCacheAttention listing of the jsqmd.com page does with its concatenation. */
@@ -134,7 +136,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *   (layout: pa_decode_workspace_bytes); `out` is not touched and may be NULL.
  *   pa_reduce then merges the partials into out.
  * max_context_len bounds every context length and must not exceed
- * 16 * max_blocks_per_seq. */
+ * bs * max_blocks_per_seq.  Partition sizes are multiples of 16 tokens for
+ * either block size. */
 pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
                     const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
@@ -178,15 +181,16 @@ pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t 
                     int32_t partition_size, int32_t out_dtype, void* out, hipStream_t stream);
 
 /* The gather indices pa_decode uses, computed by the same device function:
- * slot_ids[s][t] = block_tables[s][t / 16] * 16 + t % 16 for t < context_lens[s]
- * (after the same clamping), -1 for context_lens[s] <= t < max_context_len.
- * slot_ids is int64 [num_seqs][max_context_len].  Used to check the block-table
- * arithmetic bit for bit (the worked example of §3.2 of the ialgorithm.me page).
- * num_blocks is the pool size used for clamping. */
+ * slot_ids[s][t] = block_tables[s][t / bs] * bs + t % bs for t < context_lens[s]
+ * (after the same clamping), -1 for context_lens[s] <= t < max_context_len,
+ * with bs = block_size (16 or 8).  slot_ids is int64 [num_seqs][max_context_len].
+ * Used to check the block-table arithmetic bit for bit (the worked example of
+ * §3.2 of the ialgorithm.me page).  num_blocks is the pool size used for
+ * clamping. */
 pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t num_seqs,
-                            int32_t max_context_len, int32_t num_blocks, int64_t* slot_ids,
-                            hipStream_t stream);
+                            int32_t max_context_len, int32_t num_blocks, int32_t block_size,
+                            int64_t* slot_ids, hipStream_t stream);
 
 /* Quantised key cache (§4.2 of the blog.tanteng.space page: keys quantised
  * per channel, values kept in 16-bit; "KV Cache量化" of the ybb.press page:
@@ -230,7 +234,7 @@ pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
  * moves a request's blocks out to host memory and back later).
  * pa_gather_blocks packs blocks block_ids[0 .. n) of both pools contiguously:
  * block i goes to k_dst / v_dst at byte offset i * block_bytes, block_bytes =
- * num_kv_heads * 16 * head_dim * element size of that pool (the pool's own
+ * num_kv_heads * bs * head_dim * element size of that pool (the pool's own
  * tile order; 1 byte for int8 keys).
  * pa_scatter_blocks is the inverse: k_src / v_src block i goes to pool block
  * block_ids[i].  block_ids is int32 in device memory; ids outside the pool are

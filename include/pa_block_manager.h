@@ -1,7 +1,7 @@
 /*
  * pa_block_manager.h -- host-side allocator of the paged KV pool.
  *
- * The block manager decides which physical 16-token block holds which tokens
+ * The block manager decides which physical block (16 or 8 tokens) holds which tokens
  * of which sequence; the kernels of pa.h only read and write the blocks it
  * hands out.  What it implements is the block scheduling of the pages
  *   "LLM 推理优化：KV Cache、PagedAttention 与量化" (blog.tanteng.space),
@@ -26,11 +26,12 @@
  *  - Releasing a sequence walks its table from its last block to its first.
  *  - A full block's content key is the whole token prefix up to its end, held
  *    as a chained 64-bit FNV-1a hash: chain(prev, block) = FNV-1a over the 8
- *    little-endian bytes of prev followed by the 16 token ids as 4-byte
+ *    little-endian bytes of prev followed by the block's token ids as 4-byte
  *    little-endian integers; the empty prefix has chain 0.  The map key is
- *    (chain of the previous block, the 16 token ids), compared exactly.
- *  - A prefix lookup matches at most (n - 1) / 16 full blocks of an n-token
- *    prompt, so the last prompt token is always left for the model.
+ *    (chain of the previous block, the block's token ids), compared exactly.
+ *  - A prefix lookup matches at most (n - 1) / bs full blocks of an n-token
+ *    prompt (bs = tokens per block), so the last prompt token is always left
+ *    for the model.
  *  - Only the first token of an append can land in a partially filled block
  *    shared with another table; that block is copied (at most one copy per
  *    append) and the copy is reported for the caller to perform with
@@ -70,8 +71,11 @@ typedef struct pa_bm_stats {
   int64_t evictions;        /* cached blocks evicted so far */
 } pa_bm_stats;
 
-/* A manager for a pool of num_blocks physical blocks (num_blocks > 0). */
-pa_status pa_bm_create(int32_t num_blocks, pa_block_manager** out);
+/* A manager for a pool of num_blocks physical blocks (num_blocks > 0) of
+ * block_size tokens: 16 (the pages' default) or 8 (the smaller blocks §2.2
+ * of the blog.tanteng.space page mentions for 70B models); other sizes give
+ * PA_ERR_UNSUPPORTED.  Slots are physical * block_size + offset. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager** out);
 void pa_bm_destroy(pa_block_manager* bm);
 
 /* A new empty sequence.  hashing != 0: the full blocks it writes are registered
@@ -80,12 +84,12 @@ pa_status pa_bm_add_seq(pa_block_manager* bm, int64_t seq_id, int32_t hashing);
 
 /* Prefix sharing (§2.3 (3)): for an empty hashing sequence, share the
  * registered blocks that begin prompt[0 .. n); *cached_tokens = tokens now in
- * its table (a multiple of 16, at most 16 * ((n - 1) / 16)).  The caller then
+ * its table (a multiple of the block size bs, at most bs * ((n - 1) / bs)).  The caller then
  * appends the remaining prompt tokens. */
 pa_status pa_bm_match_prefix(pa_block_manager* bm, int64_t seq_id, const int32_t* prompt,
                              int32_t n, int32_t* cached_tokens);
 
-/* Slots for n new tokens of a sequence: slots[i] = physical * 16 + offset of
+/* Slots for n new tokens of a sequence: slots[i] = physical * bs + offset of
  * token len + i (int64, the slot_mapping of pa_write_kv).  token_ids: the n
  * token ids (required for registration; NULL stops hashing for this sequence
  * from here on).  copy_src_dst[0..1] = (source, destination) block of a
@@ -113,7 +117,7 @@ pa_status pa_bm_free_seq(pa_block_manager* bm, int64_t seq_id);
  * into `table` (*num_blocks = its length, *context_len = the length) and then
  * releases it as pa_bm_free_seq does; the sequence keeps its length and hashing
  * state.  The caller saves the listed blocks' contents (pa_gather_blocks)
- * before anything else writes to the pool.  swap_in: ceil(len / 16) fresh
+ * before anything else writes to the pool.  swap_in: ceil(len / bs) fresh
  * blocks, all or nothing (PA_ERR_NO_SPACE), written to `table`; the caller
  * restores the contents there (pa_scatter_blocks).  PA_ERR_INVALID_ARG when
  * capacity is too small (nothing changes). */

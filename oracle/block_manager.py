@@ -37,7 +37,9 @@ result unique, so the C++ manager can be compared with this model exactly):
 * Content identity of a full block is the whole token prefix up to its end (the
   K/V of a token depend on every token before it).  Here the key *is* that
   prefix; the library keys a chained hash of it.
-* A lookup never covers the last prompt token: at most (n - 1) // 16 full
+* Blocks hold 16 tokens (the pages' default) or 8 (the variant of §2.2); the
+  model takes either.
+* A lookup never covers the last prompt token: at most (n - 1) // bs full
   blocks are matched, so at least one prompt token is computed by the model
   (its logits are needed).
 * The first token of an append may land in a partially filled block that other
@@ -58,9 +60,10 @@ class PoolExhausted(Exception):
 
 
 class BlockManagerModel:
-    def __init__(self, num_blocks: int):
-        assert num_blocks > 0
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        assert num_blocks > 0 and block_size in (8, 16)
         self.num_blocks = num_blocks
+        self.bs = block_size
         self.free = list(range(num_blocks - 1, -1, -1))  # stack: pop() gives 0 first
         self.ref = [0] * num_blocks
         self.key_of = {}          # block -> token prefix tuple it holds (registered blocks)
@@ -105,9 +108,9 @@ class BlockManagerModel:
         of tokens now cached for ``seq`` (a multiple of 16)."""
         assert self.lens[seq] == 0 and self.tokens[seq] is not None
         prompt = list(prompt)
-        n_blocks = max(len(prompt) - 1, 0) // BLOCK_SIZE
+        n_blocks = max(len(prompt) - 1, 0) // self.bs
         for i in range(n_blocks):
-            key = tuple(prompt[: (i + 1) * BLOCK_SIZE])
+            key = tuple(prompt[: (i + 1) * self.bs])
             b = self.block_of.get(key)
             if b is None:
                 break
@@ -115,14 +118,14 @@ class BlockManagerModel:
                 del self.cached[b]
             self.ref[b] += 1
             self.tables[seq].append(b)
-            self.lens[seq] += BLOCK_SIZE
-            self.tokens[seq].extend(prompt[i * BLOCK_SIZE:(i + 1) * BLOCK_SIZE])
+            self.lens[seq] += self.bs
+            self.tokens[seq].extend(prompt[i * self.bs:(i + 1) * self.bs])
         return self.lens[seq]
 
     def blocks_needed(self, seq: int, n: int) -> int:
         L = self.lens[seq]
-        new = -(-(L + n) // BLOCK_SIZE) - (-(-L // BLOCK_SIZE))
-        cow = 1 if (n > 0 and L % BLOCK_SIZE != 0 and self.ref[self.tables[seq][-1]] > 1) else 0
+        new = -(-(L + n) // self.bs) - (-(-L // self.bs))
+        cow = 1 if (n > 0 and L % self.bs != 0 and self.ref[self.tables[seq][-1]] > 1) else 0
         return new + cow
 
     def append(self, seq: int, n: int, token_ids=None):
@@ -137,7 +140,7 @@ class BlockManagerModel:
         slots, copy = [], None
         for i in range(n):
             t = self.lens[seq]
-            if t % BLOCK_SIZE == 0:
+            if t % self.bs == 0:
                 b = self._take()
                 self.ref[b] = 1
                 table.append(b)
@@ -148,13 +151,13 @@ class BlockManagerModel:
                 self.ref[src] -= 1              # still referenced by another table
                 table[-1] = dst
                 copy = (src, dst)
-            slots.append(table[t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE)
+            slots.append(table[t // self.bs] * self.bs + t % self.bs)
             self.lens[seq] = t + 1
             if toks is not None:
                 toks.append(int(token_ids[i]))
-                if (t + 1) % BLOCK_SIZE == 0:
+                if (t + 1) % self.bs == 0:
                     key = tuple(toks)
-                    b = table[t // BLOCK_SIZE]
+                    b = table[t // self.bs]
                     if key not in self.block_of and b not in self.key_of:
                         self.block_of[key] = b
                         self.key_of[b] = key
@@ -195,7 +198,7 @@ class BlockManagerModel:
         nothing; returns its new table (where the caller copies the contents back).
         The fresh blocks are not registered for prefix sharing."""
         L, toks = self.swapped[seq]
-        need = -(-L // BLOCK_SIZE)
+        need = -(-L // self.bs)
         if need > self.available():
             raise PoolExhausted()
         del self.swapped[seq]

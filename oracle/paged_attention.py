@@ -63,44 +63,47 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
 # --------------------------------------------------------------------------
 # block-table address arithmetic  [P3 §2.2; P4 §3.2 block-table figure]
 # --------------------------------------------------------------------------
-def slot_of(table_row: np.ndarray, t: int) -> int:
-    """Token t sits in logical block t // 16 at offset t % 16; the table maps the
-    logical block to a physical one; the slot is physical * 16 + offset."""
-    logical = t // BLOCK_SIZE
-    offset = t % BLOCK_SIZE
+def slot_of(table_row: np.ndarray, t: int, block_size: int = BLOCK_SIZE) -> int:
+    """Token t sits in logical block t // bs at offset t % bs (bs = 16 by default;
+    the 8-token variant of [P3] §2.2 as well); the table maps the logical block to
+    a physical one; the slot is physical * bs + offset."""
+    logical = t // block_size
+    offset = t % block_size
     physical = int(table_row[logical])
-    return physical * BLOCK_SIZE + offset
+    return physical * block_size + offset
 
 
-def slot_ids(block_tables: np.ndarray, context_lens: np.ndarray, max_context_len: int) -> np.ndarray:
+def slot_ids(block_tables: np.ndarray, context_lens: np.ndarray, max_context_len: int,
+             block_size: int = BLOCK_SIZE) -> np.ndarray:
     """int64 [B][max_context_len]: the slot of every live token, -1 past the length."""
     B = len(context_lens)
     out = np.full((B, max_context_len), -1, dtype=np.int64)
     for s in range(B):
         for t in range(min(int(context_lens[s]), max_context_len)):
-            out[s, t] = slot_of(block_tables[s], t)
+            out[s, t] = slot_of(block_tables[s], t, block_size)
     return out
 
 
 def tile_byte_offset(physical: int, kv_head: int, num_kv_heads: int, head_dim: int,
-                     elem_bytes: int) -> int:
-    """Byte offset of tile (physical block, kv head) in a pool of 16 * d-element
+                     elem_bytes: int, block_size: int = BLOCK_SIZE) -> int:
+    """Byte offset of tile (physical block, kv head) in a pool of bs * d-element
     tiles ordered block-major, then by KV head."""
-    tile_bytes = BLOCK_SIZE * head_dim * elem_bytes
+    tile_bytes = block_size * head_dim * elem_bytes
     return (physical * num_kv_heads + kv_head) * tile_bytes
 
 
 # Pool layouts (the library's ABI; only the order of elements inside a tile
-# differs between K and V):
-#   K  [blocks][H_kv][d / x][16][x]   x = elements per 16-byte chunk: element c
+# differs between K and V; bs = tokens per block, read from the pool's shape):
+#   K  [blocks][H_kv][d / x][bs][x]   x = elements per 16-byte chunk: element c
 #                                      of the token at offset o is at [c // x][o][c % x]
-#   V  [blocks][H_kv][d][16]          element c of the token at offset o is at [c][o]
+#   V  [blocks][H_kv][d][bs]          element c of the token at offset o is at [c][o]
 def k_rows(k_pool: np.ndarray, table_row: np.ndarray, length: int, kv_head: int) -> np.ndarray:
     """K rows [length][d] (stored dtype) of one KV head of one sequence, in token
-    order: row t comes from physical block table_row[t // 16] at offset t % 16."""
+    order: row t comes from physical block table_row[t // bs] at offset t % bs."""
+    bs = k_pool.shape[3]
     t = np.arange(length)
-    physical = table_row[t // BLOCK_SIZE]
-    offset = t % BLOCK_SIZE
+    physical = table_row[t // bs]
+    offset = t % bs
     n_chunks, x = k_pool.shape[2], k_pool.shape[4]
     rows = np.empty((length, n_chunks, x), dtype=k_pool.dtype)
     for c in range(n_chunks):
@@ -109,10 +112,11 @@ def k_rows(k_pool: np.ndarray, table_row: np.ndarray, length: int, kv_head: int)
 
 
 def v_rows(v_pool: np.ndarray, table_row: np.ndarray, length: int, kv_head: int) -> np.ndarray:
-    """V rows [length][d] (stored dtype), in token order, from the [d][16] tiles."""
+    """V rows [length][d] (stored dtype), in token order, from the [d][bs] tiles."""
+    bs = v_pool.shape[3]
     t = np.arange(length)
-    physical = table_row[t // BLOCK_SIZE]
-    offset = t % BLOCK_SIZE
+    physical = table_row[t // bs]
+    offset = t % bs
     d = v_pool.shape[2]
     rows = np.empty((length, d), dtype=v_pool.dtype)
     for c in range(d):
@@ -238,16 +242,16 @@ def merge_partials(o_part: np.ndarray, lse_part: np.ndarray) -> np.ndarray:
 def write_kv(k_pool, v_pool, k_new, v_new, slot_mapping):
     """Copies of the pools with token i's [H_kv][d] rows stored at slot_mapping[i].
 
-    A slot is physical * 16 + offset; negative slots are skipped.  Values are
+    A slot is physical * bs + offset; negative slots are skipped.  Values are
     copied bit for bit into the K and V tile layouts described above.
     """
     k_out = k_pool.copy()
     v_out = v_pool.copy()
-    n_kv, n_chunks, x = k_pool.shape[1], k_pool.shape[2], k_pool.shape[4]
+    n_kv, n_chunks, bs, x = k_pool.shape[1], k_pool.shape[2], k_pool.shape[3], k_pool.shape[4]
     for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
         if slot < 0:
             continue
-        b, o = divmod(int(slot), BLOCK_SIZE)
+        b, o = divmod(int(slot), bs)
         for g in range(n_kv):
             for c in range(n_chunks * x):
                 k_out[b, g, c // x, o, c % x] = k_new[i, g, c]

@@ -31,7 +31,7 @@ Readings (each listed in the design doc):
   precision.
 * Values stay in the pool's 16-bit type; q and out share it.
 
-Layout: the int8 K pool is [num_blocks][H_kv][d / 16][16][16] -- the same
+Layout: the int8 K pool is [num_blocks][H_kv][d / 16][bs][16] -- the same
 chunk-major tile order as the 16-bit K pool with 16 elements per 16-byte
 chunk -- and the scales are float32 [H_kv][d].
 """
@@ -57,8 +57,8 @@ def dequantize_k(codes: np.ndarray, k_scale: np.ndarray) -> np.ndarray:
     return codes.astype(np.float64) * np.asarray(k_scale, dtype=np.float32).astype(np.float64)
 
 
-def k8_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int):
-    return (num_blocks, num_kv_heads, head_dim // 16, BLOCK_SIZE, 16)
+def k8_pool_shape(num_blocks: int, num_kv_heads: int, head_dim: int, block_size: int = BLOCK_SIZE):
+    return (num_blocks, num_kv_heads, head_dim // 16, block_size, 16)
 
 
 def write_kv_k8(k8_pool, v_pool, k_scale, k_new, v_new, slot_mapping, dtype):
@@ -68,10 +68,11 @@ def write_kv_k8(k8_pool, v_pool, k_scale, k_new, v_new, slot_mapping, dtype):
     k_out, v_out = k8_pool.copy(), v_pool.copy()
     codes = quantize_k(k_new, k_scale, dtype)
     n_kv, d = k_new.shape[1], k_new.shape[2]
+    bs = k8_pool.shape[3]
     for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
         if slot < 0:
             continue
-        b, o = divmod(int(slot), BLOCK_SIZE)
+        b, o = divmod(int(slot), bs)
         for g in range(n_kv):
             for c in range(d):
                 k_out[b, g, c // 16, o, c % 16] = codes[i, g, c]

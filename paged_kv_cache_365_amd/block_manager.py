@@ -41,7 +41,7 @@ def _lib():
     if not _bound:
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         sig = {
-            "pa_bm_create": [i32, vp],
+            "pa_bm_create": [i32, i32, vp],
             "pa_bm_add_seq": [vp, i64, i32],
             "pa_bm_match_prefix": [vp, i64, vp, i32, vp],
             "pa_bm_append": [vp, i64, vp, i32, vp, vp],
@@ -78,12 +78,14 @@ def _i32(x) -> np.ndarray:
 class BlockManager:
     """Owner of one ``pa_block_manager`` handle."""
 
-    def __init__(self, num_blocks: int):
+    def __init__(self, num_blocks: int, block_size: int = 16):
         self._lib = _lib()
         h = ctypes.c_void_p()
-        pa._check("pa_bm_create", self._lib.pa_bm_create(int(num_blocks), ctypes.byref(h)))
+        pa._check("pa_bm_create", self._lib.pa_bm_create(int(num_blocks), int(block_size),
+                                                         ctypes.byref(h)))
         self._h = h
         self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -32,14 +32,14 @@ int k_elem_bytes(int32_t dtype) { return is_k8(dtype) ? 1 : elem_bytes(dtype); }
 pa_status check_pool(const pa_pool_desc* pool) {
   if (!pool) return PA_ERR_INVALID_ARG;
   if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0) return PA_ERR_INVALID_ARG;
-  if (pool->block_size != pa::kBlockSize) return PA_ERR_UNSUPPORTED;
+  if (pool->block_size != 16 && pool->block_size != 8) return PA_ERR_UNSUPPORTED;
   if (pool->head_dim != 64 && pool->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (elem_bytes(pool->dtype) == 0) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
 size_t block_elems(const pa_pool_desc* pool) {
-  return static_cast<size_t>(pool->num_kv_heads) * pa::kBlockSize * pool->head_dim;
+  return static_cast<size_t>(pool->num_kv_heads) * pool->block_size * pool->head_dim;
 }
 size_t k_pool_bytes(const pa_pool_desc* pool) {
   return pool->num_blocks * block_elems(pool) * k_elem_bytes(pool->dtype);
@@ -103,8 +103,8 @@ pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, cons
     return PA_ERR_MISALIGNED;
   const int row_bytes = pool->head_dim * elem_bytes(pool->dtype);
   return from_hip(pa::launch_write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens,
-                                      pool->num_blocks, pool->num_kv_heads, row_bytes,
-                                      elem_bytes(pool->dtype), stream));
+                                      pool->num_blocks, pool->block_size, pool->num_kv_heads,
+                                      row_bytes, elem_bytes(pool->dtype), stream));
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -140,9 +140,9 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
     return PA_ERR_INVALID_ARG;
   if (num_query_tokens < 1 || num_query_tokens > kMaxQueryTokens) return PA_ERR_INVALID_ARG;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * pa::kBlockSize)
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * pool->block_size)
     return PA_ERR_INVALID_ARG;
-  if (partition_size < 0 || partition_size % pa::kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (partition_size < 0 || partition_size % pa::kStep != 0) return PA_ERR_INVALID_ARG;
   // one workgroup per 16 (query token, head) rows at most, per KV head, sequence
   // and partition: the one-dimensional grid must count them in 31 bits
   const int64_t rows = static_cast<int64_t>(num_query_tokens) * (num_q_heads / pool->num_kv_heads);
@@ -167,6 +167,7 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
   a.num_kv_heads = pool->num_kv_heads;
   a.head_dim = pool->head_dim;
   a.num_blocks = pool->num_blocks;
+  a.block_size = pool->block_size;
   a.max_context_len = max_context_len;
   a.dtype = pool->dtype;
   a.scale = scale;
@@ -176,9 +177,9 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
     if (!out) return PA_ERR_INVALID_ARG;
     if (!aligned(out, 16)) return PA_ERR_MISALIGNED;
     // one partition spanning every context
-    const int64_t span = (static_cast<int64_t>(max_context_len) + pa::kBlockSize - 1) /
-                         pa::kBlockSize * pa::kBlockSize;
-    a.partition_tokens = static_cast<int32_t>(span < pa::kBlockSize ? pa::kBlockSize : span);
+    const int64_t span = (static_cast<int64_t>(max_context_len) + pa::kStep - 1) / pa::kStep *
+                         pa::kStep;
+    a.partition_tokens = static_cast<int32_t>(span < pa::kStep ? pa::kStep : span);
     a.num_parts = 1;
     a.write_partials = false;
     a.out = out;
@@ -251,8 +252,8 @@ pa_status pa_write_kv_k8(const pa_pool_desc* pool, void* k_pool, void* v_pool, c
       !aligned(slot_mapping, 8) || !aligned(k_scale, 4))
     return PA_ERR_MISALIGNED;
   return from_hip(pa::launch_write_kv_k8(k_pool, v_pool, k_scale, k_new, v_new, slot_mapping,
-                                         num_tokens, pool->num_blocks, pool->num_kv_heads,
-                                         pool->head_dim, pool->dtype, stream));
+                                         num_tokens, pool->num_blocks, pool->block_size,
+                                         pool->num_kv_heads, pool->head_dim, pool->dtype, stream));
 }
 
 pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,
@@ -260,7 +261,7 @@ pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t 
                     int32_t partition_size, int32_t out_dtype, void* out, hipStream_t stream) {
   if (!workspace || !context_lens || !out) return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
-  if (partition_size <= 0 || partition_size % pa::kBlockSize != 0) return PA_ERR_INVALID_ARG;
+  if (partition_size <= 0 || partition_size % pa::kStep != 0) return PA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (elem_bytes(out_dtype) == 0 || is_k8(out_dtype)) return PA_ERR_UNSUPPORTED;
   if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
@@ -369,18 +370,19 @@ pa_status pa_scatter_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool
 
 pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t num_seqs,
-                            int32_t max_context_len, int32_t num_blocks, int64_t* slot_ids,
-                            hipStream_t stream) {
+                            int32_t max_context_len, int32_t num_blocks, int32_t block_size,
+                            int64_t* slot_ids, hipStream_t stream) {
   if (!block_tables || !context_lens || !slot_ids) return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * pa::kBlockSize)
+  if (block_size != 16 && block_size != 8) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PA_ERR_INVALID_ARG;
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(slot_ids, 8))
     return PA_ERR_MISALIGNED;
   if (max_context_len == 0) return PA_OK;
   return from_hip(pa::launch_slot_ids(block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                                      max_context_len, num_blocks, slot_ids, stream));
+                                      max_context_len, num_blocks, block_size, slot_ids, stream));
 }
 
 }  // extern "C"

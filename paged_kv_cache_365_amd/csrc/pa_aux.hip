@@ -116,19 +116,20 @@ __global__ __launch_bounds__(256) void fill_kernel(uint4* dst, size_t n16, uint3
 // ---------------------------------------------------------------------------
 // write_kv: token i's [H_kv][d] K and V rows go to slot slot_mapping[i]; one
 // thread per 16-byte chunk of an input row, a plain copy of bits into the tile
-// layouts: K tiles are [d / x][16][x] (the chunk lands whole at (chunk, offset)),
-// V tiles are [d][16] (the chunk's x elements land in x different columns).
+// layouts of bs-token blocks: K tiles are [d / x][bs][x] (the chunk lands whole
+// at (chunk, offset)), V tiles are [d][bs] (the chunk's x elements land in x
+// different columns).
 // ---------------------------------------------------------------------------
 template <typename E>
 __global__ __launch_bounds__(256) void write_kv_kernel(char* k_pool, char* v_pool,
                                                        const uint4* k_new, const uint4* v_new,
                                                        const int64_t* slot_mapping, int num_tokens,
-                                                       int64_t num_slots, int num_kv_heads,
+                                                       int64_t num_slots, int bs, int num_kv_heads,
                                                        int chunks_per_row) {
   constexpr int kX = 16 / sizeof(E);  // elements per chunk
   const int chunks_per_token = num_kv_heads * chunks_per_row;
   const int64_t total = static_cast<int64_t>(num_tokens) * chunks_per_token;
-  const size_t tile_bytes = static_cast<size_t>(kBlockSize) * chunks_per_row * 16;
+  const size_t tile_bytes = static_cast<size_t>(bs) * chunks_per_row * 16;
   for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < total;
        idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int tok = static_cast<int>(idx / chunks_per_token);
@@ -137,16 +138,16 @@ __global__ __launch_bounds__(256) void write_kv_kernel(char* k_pool, char* v_poo
     const int rem = static_cast<int>(idx % chunks_per_token);
     const int g = rem / chunks_per_row;
     const int ch = rem % chunks_per_row;
-    const int64_t phys = slot / kBlockSize;
-    const int o = static_cast<int>(slot % kBlockSize);
+    const int64_t phys = slot / bs;
+    const int o = static_cast<int>(slot % bs);
     const size_t tile = (static_cast<size_t>(phys) * num_kv_heads + g) * tile_bytes;
-    *reinterpret_cast<uint4*>(k_pool + tile + (static_cast<size_t>(ch) * kBlockSize + o) * 16) = k_new[idx];
+    *reinterpret_cast<uint4*>(k_pool + tile + (static_cast<size_t>(ch) * bs + o) * 16) = k_new[idx];
     const uint4 v = v_new[idx];
     E e[kX];
     __builtin_memcpy(e, &v, 16);
     E* vt = reinterpret_cast<E*>(v_pool + tile);
 #pragma unroll
-    for (int i = 0; i < kX; ++i) vt[(ch * kX + i) * kBlockSize + o] = e[i];
+    for (int i = 0; i < kX; ++i) vt[(ch * kX + i) * bs + o] = e[i];
   }
 }
 
@@ -156,14 +157,14 @@ __global__ __launch_bounds__(256) void write_kv_kernel(char* k_pool, char* v_poo
 // IEEE float32 division rounded to nearest and rint rounding ties to even.
 // One thread per 16 channels of one token and KV head: two 16-byte loads of
 // the 16-bit key row, one 16-byte store of codes into the int8 tile
-// ([d / 16][16][16]); the 16 value elements land in 16 columns of the V tile.
+// ([d / 16][bs][16]); the 16 value elements land in 16 columns of the V tile.
 // ---------------------------------------------------------------------------
 template <class Tr, typename E>
 __global__ __launch_bounds__(256) void write_kv_k8_kernel(char* k_pool, char* v_pool,
                                                           const float* k_scale,
                                                           const uint4* k_new, const uint4* v_new,
                                                           const int64_t* slot_mapping,
-                                                          int num_tokens, int64_t num_slots,
+                                                          int num_tokens, int64_t num_slots, int bs,
                                                           int num_kv_heads, int head_dim) {
   const int groups = head_dim / 16;  // 16-channel groups per row
   const int per_token = num_kv_heads * groups;
@@ -176,9 +177,9 @@ __global__ __launch_bounds__(256) void write_kv_k8_kernel(char* k_pool, char* v_
     const int rem = static_cast<int>(idx % per_token);
     const int g = rem / groups;
     const int cg = rem % groups;
-    const int64_t phys = slot / kBlockSize;
-    const int o = static_cast<int>(slot % kBlockSize);
-    const size_t tile = (static_cast<size_t>(phys) * num_kv_heads + g) * kBlockSize * head_dim;
+    const int64_t phys = slot / bs;
+    const int o = static_cast<int>(slot % bs);
+    const size_t tile = (static_cast<size_t>(phys) * num_kv_heads + g) * bs * head_dim;
     const size_t row = (static_cast<size_t>(tok) * num_kv_heads + g) * head_dim + 16 * cg;  // elements
     float kf[16];
     Tr::unpack(k_new[row / 8], kf);
@@ -192,14 +193,14 @@ __global__ __launch_bounds__(256) void write_kv_k8_kernel(char* k_pool, char* v_
       const uint32_t b = static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xffu;
       w[e / 4] |= b << (8 * (e % 4));
     }
-    *reinterpret_cast<uint4*>(k_pool + tile + (static_cast<size_t>(cg) * kBlockSize + o) * 16) =
+    *reinterpret_cast<uint4*>(k_pool + tile + (static_cast<size_t>(cg) * bs + o) * 16) =
         make_uint4(w[0], w[1], w[2], w[3]);
     E ve[16];
     __builtin_memcpy(ve, &v_new[row / 8], 16);
     __builtin_memcpy(ve + 8, &v_new[row / 8 + 1], 16);
     E* vt = reinterpret_cast<E*>(v_pool) + tile;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) vt[(16 * cg + e) * kBlockSize + o] = ve[e];
+    for (int e = 0; e < 16; ++e) vt[(16 * cg + e) * bs + o] = ve[e];
   }
 }
 
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void block_move_kernel(const uint4* src_k, con
 __global__ __launch_bounds__(256) void slot_ids_kernel(const int32_t* block_tables,
                                                        int max_blocks_per_seq,
                                                        const int32_t* context_lens, int num_seqs,
-                                                       int max_context_len, int num_blocks,
+                                                       int max_context_len, int num_blocks, int bs,
                                                        int64_t* slot_ids) {
   const int64_t total = static_cast<int64_t>(num_seqs) * max_context_len;
   for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < total;
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void slot_ids_kernel(const int32_t* block_tabl
     int64_t v = -1;
     if (t < L) {
       const int32_t* row = block_tables + static_cast<size_t>(s) * max_blocks_per_seq;
-      v = pa_slot(pa_physical_block(row, t / kBlockSize, num_blocks), t);
+      v = pa_slot(pa_physical_block(row, t / bs, num_blocks), t, bs);
     }
     slot_ids[idx] = v;
   }
@@ -283,31 +284,31 @@ hipError_t launch_fill(void* dst, size_t bytes, uint32_t pattern, hipStream_t st
 
 hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                           int32_t num_kv_heads, int32_t row_bytes, int32_t elem_bytes,
-                           hipStream_t stream) {
+                           int32_t block_size, int32_t num_kv_heads, int32_t row_bytes,
+                           int32_t elem_bytes, hipStream_t stream) {
   const int chunks_per_row = row_bytes / 16;
   const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * chunks_per_row;
   auto kernel = elem_bytes == 4 ? write_kv_kernel<uint32_t> : write_kv_kernel<uint16_t>;
   hipLaunchKernelGGL(kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
                      static_cast<char*>(k_pool), static_cast<char*>(v_pool),
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
-                     slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * kBlockSize,
-                     num_kv_heads, chunks_per_row);
+                     slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * block_size,
+                     block_size, num_kv_heads, chunks_per_row);
   return hipGetLastError();
 }
 
 hipError_t launch_write_kv_k8(void* k_pool, void* v_pool, const float* k_scale, const void* k_new,
                               const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
-                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t dtype, hipStream_t stream) {
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t dtype, hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 16);
   auto kernel = dtype == PA_K8_F16 ? write_kv_k8_kernel<F16, uint16_t>
                                    : write_kv_k8_kernel<BF16, uint16_t>;
   hipLaunchKernelGGL(kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
                      static_cast<char*>(k_pool), static_cast<char*>(v_pool), k_scale,
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
-                     slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * kBlockSize,
-                     num_kv_heads, head_dim);
+                     slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * block_size,
+                     block_size, num_kv_heads, head_dim);
   return hipGetLastError();
 }
 
@@ -327,11 +328,12 @@ hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream) {
 
 hipError_t launch_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-                           int32_t num_blocks, int64_t* slot_ids, hipStream_t stream) {
+                           int32_t num_blocks, int32_t block_size, int64_t* slot_ids,
+                           hipStream_t stream) {
   const int64_t total = static_cast<int64_t>(num_seqs) * max_context_len;
   hipLaunchKernelGGL(slot_ids_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
                      block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len,
-                     num_blocks, slot_ids);
+                     num_blocks, block_size, slot_ids);
   return hipGetLastError();
 }
 

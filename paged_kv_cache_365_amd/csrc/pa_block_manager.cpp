@@ -22,19 +22,19 @@
 
 namespace {
 
-constexpr int kBs = 16;  // tokens per block
+constexpr int kMaxBs = 16;  // tokens per block: 16, or 8
 constexpr uint64_t kFnvOffset = 0xcbf29ce484222325ull;
 constexpr uint64_t kFnvPrime = 0x100000001b3ull;
 
-// FNV-1a over the 8 little-endian bytes of prev, then 16 int32 token ids as
-// 4 little-endian bytes each.
-uint64_t chain_hash(uint64_t prev, const int32_t* tok) {
+// FNV-1a over the 8 little-endian bytes of prev, then the block's bs int32
+// token ids as 4 little-endian bytes each.
+uint64_t chain_hash(uint64_t prev, const int32_t* tok, int bs) {
   uint64_t h = kFnvOffset;
   for (int i = 0; i < 8; ++i) {
     h ^= (prev >> (8 * i)) & 0xffu;
     h *= kFnvPrime;
   }
-  for (int t = 0; t < kBs; ++t) {
+  for (int t = 0; t < bs; ++t) {
     const uint32_t u = static_cast<uint32_t>(tok[t]);
     for (int i = 0; i < 4; ++i) {
       h ^= (u >> (8 * i)) & 0xffu;
@@ -45,28 +45,32 @@ uint64_t chain_hash(uint64_t prev, const int32_t* tok) {
 }
 
 struct Key {
-  uint64_t prev;       // chain of the prefix before this block
-  int32_t tok[kBs];    // the block's token ids
+  uint64_t prev;          // chain of the prefix before this block
+  int32_t tok[kMaxBs];    // the block's token ids (entries past the block size are 0)
+  int32_t bs;
   bool operator==(const Key& o) const {
     return prev == o.prev && memcmp(tok, o.tok, sizeof(tok)) == 0;
   }
 };
 struct KeyHash {
-  size_t operator()(const Key& k) const { return static_cast<size_t>(chain_hash(k.prev, k.tok)); }
+  size_t operator()(const Key& k) const {
+    return static_cast<size_t>(chain_hash(k.prev, k.tok, k.bs));
+  }
 };
 
 struct Seq {
   std::vector<int32_t> table;
   int32_t len = 0;
   bool hashing = false;
-  uint64_t chain = 0;      // chain of the last full block (0 = empty prefix)
-  int32_t cur[kBs] = {0};  // token ids of the current partial block
+  uint64_t chain = 0;         // chain of the last full block (0 = empty prefix)
+  int32_t cur[kMaxBs] = {0};  // token ids of the current partial block
 };
 
 }  // namespace
 
 struct pa_block_manager {
   int32_t num_blocks;
+  int32_t bs;  // tokens per block
   std::vector<int32_t> ref;
   std::vector<int32_t> free_stack;
   // LRU list of cached (unreferenced, registered) blocks: head = oldest
@@ -81,8 +85,8 @@ struct pa_block_manager {
   std::unordered_map<int64_t, Seq> swapped;  // table empty while swapped out
   int64_t prefix_hits = 0, cow_copies = 0, evictions = 0;
 
-  explicit pa_block_manager(int32_t n)
-      : num_blocks(n), ref(n, 0), lru_prev(n, -1), lru_next(n, -1), in_lru(n, 0),
+  pa_block_manager(int32_t n, int32_t block_size)
+      : num_blocks(n), bs(block_size), ref(n, 0), lru_prev(n, -1), lru_next(n, -1), in_lru(n, 0),
         registered(n, 0), key_of(n) {
     free_stack.reserve(n);
     for (int32_t b = n - 1; b >= 0; --b) free_stack.push_back(b);
@@ -129,14 +133,23 @@ struct pa_block_manager {
     }
   }
 
-  static int32_t div_up(int64_t x) { return static_cast<int32_t>((x + kBs - 1) / kBs); }
+  int32_t div_up(int64_t x) const { return static_cast<int32_t>((x + bs - 1) / bs); }
 
   int32_t blocks_needed(const Seq& s, int32_t n) const {
     if (n <= 0) return 0;
     const int64_t L = s.len;
     int32_t need = div_up(L + n) - div_up(L);
-    if (L % kBs != 0 && ref[s.table.back()] > 1) need += 1;  // copy-on-write
+    if (L % bs != 0 && ref[s.table.back()] > 1) need += 1;  // copy-on-write
     return need;
+  }
+
+  Key make_key(uint64_t prev, const int32_t* tok) const {
+    Key k;
+    k.prev = prev;
+    k.bs = bs;
+    memset(k.tok, 0, sizeof(k.tok));
+    memcpy(k.tok, tok, sizeof(int32_t) * bs);
+    return k;
   }
 
   // append n tokens (availability already checked)
@@ -145,7 +158,7 @@ struct pa_block_manager {
     if (!tokens) s.hashing = false;
     for (int32_t i = 0; i < n; ++i) {
       const int32_t t = s.len;
-      const int32_t off = t % kBs;
+      const int32_t off = t % bs;
       if (off == 0) {
         const int32_t b = take();
         ref[b] = 1;
@@ -160,16 +173,14 @@ struct pa_block_manager {
         cp[1] = dst;
         ++cow_copies;
       }
-      const int32_t b = s.table[t / kBs];
-      slots[i] = static_cast<int64_t>(b) * kBs + off;
+      const int32_t b = s.table[t / bs];
+      slots[i] = static_cast<int64_t>(b) * bs + off;
       s.len = t + 1;
       if (s.hashing) {
         s.cur[off] = tokens[i];
-        if (off == kBs - 1) {
-          Key k;
-          k.prev = s.chain;
-          memcpy(k.tok, s.cur, sizeof(k.tok));
-          s.chain = chain_hash(k.prev, k.tok);
+        if (off == bs - 1) {
+          const Key k = make_key(s.chain, s.cur);
+          s.chain = chain_hash(k.prev, k.tok, bs);
           if (!registered[b] && block_of.find(k) == block_of.end()) {
             block_of.emplace(k, b);
             key_of[b] = k;
@@ -194,10 +205,12 @@ bool valid_bm(const pa_block_manager* bm) { return bm != nullptr; }
 
 extern "C" {
 
-pa_status pa_bm_create(int32_t num_blocks, pa_block_manager** out) {
-  if (!out || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager** out) {
+  if (!out) return PA_ERR_INVALID_ARG;
   *out = nullptr;
-  pa_block_manager* bm = new (std::nothrow) pa_block_manager(num_blocks);
+  if (num_blocks <= 0) return PA_ERR_INVALID_ARG;
+  if (block_size != 8 && block_size != 16) return PA_ERR_UNSUPPORTED;
+  pa_block_manager* bm = new (std::nothrow) pa_block_manager(num_blocks, block_size);
   if (!bm) return PA_ERR_NO_SPACE;
   *out = bm;
   return PA_OK;
@@ -221,22 +234,22 @@ pa_status pa_bm_match_prefix(pa_block_manager* bm, int64_t seq_id, const int32_t
   if (it == bm->seqs.end()) return PA_ERR_INVALID_ARG;
   Seq& s = it->second;
   if (s.len != 0 || !s.hashing) return PA_ERR_INVALID_ARG;
-  const int32_t max_blocks = n > 0 ? (n - 1) / kBs : 0;
-  Key k;
-  k.prev = 0;
+  const int32_t bs = bm->bs;
+  const int32_t max_blocks = n > 0 ? (n - 1) / bs : 0;
+  uint64_t prev = 0;
   for (int32_t i = 0; i < max_blocks; ++i) {
-    memcpy(k.tok, prompt + static_cast<size_t>(i) * kBs, sizeof(k.tok));
+    const Key k = bm->make_key(prev, prompt + static_cast<size_t>(i) * bs);
     auto f = bm->block_of.find(k);
     if (f == bm->block_of.end()) break;
     const int32_t b = f->second;
     if (bm->ref[b] == 0) bm->lru_remove(b);
     ++bm->ref[b];
     s.table.push_back(b);
-    s.len += kBs;
+    s.len += bs;
     ++bm->prefix_hits;
-    k.prev = chain_hash(k.prev, k.tok);
+    prev = chain_hash(prev, k.tok, bs);
   }
-  s.chain = k.prev;
+  s.chain = prev;
   *cached_tokens = s.len;
   return PA_OK;
 }
@@ -247,7 +260,7 @@ pa_status pa_bm_append(pa_block_manager* bm, int64_t seq_id, const int32_t* toke
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_INVALID_ARG;
   Seq& s = it->second;
-  if (static_cast<int64_t>(s.len) + n > INT32_MAX - kBs) return PA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(s.len) + n > INT32_MAX - kMaxBs) return PA_ERR_INVALID_ARG;
   if (bm->blocks_needed(s, n) > bm->available()) return PA_ERR_NO_SPACE;
   bm->append(s, token_ids, n, slots, copy_src_dst);
   return PA_OK;
@@ -265,7 +278,7 @@ pa_status pa_bm_append_step(pa_block_manager* bm, const int64_t* seq_ids, int32_
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end() || !seen.insert(seq_ids[i]).second) return PA_ERR_INVALID_ARG;
-    if (it->second.len > INT32_MAX - 2 * kBs) return PA_ERR_INVALID_ARG;
+    if (it->second.len > INT32_MAX - 2 * kMaxBs) return PA_ERR_INVALID_ARG;
     ss[i] = &it->second;
     need += bm->blocks_needed(it->second, 1);
   }
@@ -330,7 +343,7 @@ pa_status pa_bm_swap_in(pa_block_manager* bm, int64_t seq_id, int32_t* table, in
   auto it = bm->swapped.find(seq_id);
   if (it == bm->swapped.end()) return PA_ERR_INVALID_ARG;
   Seq& s = it->second;
-  const int32_t need = pa_block_manager::div_up(s.len);
+  const int32_t need = bm->div_up(s.len);
   if (need > capacity || (need > 0 && !table)) return PA_ERR_INVALID_ARG;
   if (need > bm->available()) return PA_ERR_NO_SPACE;
   s.table.reserve(static_cast<size_t>(need));

@@ -14,7 +14,8 @@
 
 namespace pa {
 
-constexpr int kBlockSize = 16;  // tokens per physical block
+constexpr int kBlockSize = 16;  // tokens per physical block by default (8 is also built)
+constexpr int kStep = 16;       // tokens per matrix-core step of the decode kernel
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -78,15 +79,15 @@ __device__ __forceinline__ int pa_physical_block(const int32_t* __restrict__ tab
   return b >= num_blocks ? num_blocks - 1 : b;
 }
 
-// Slot of token t held by physical block `physical`.
-__device__ __forceinline__ int64_t pa_slot(int physical, int t) {
-  return static_cast<int64_t>(physical) * kBlockSize + (t & (kBlockSize - 1));
+// Slot of token t held by physical block `physical` of a pool of bs-token blocks.
+__device__ __forceinline__ int64_t pa_slot(int physical, int t, int bs) {
+  return static_cast<int64_t>(physical) * bs + (t % bs);
 }
 
-// Element offset of tile (physical block, kv head) in a [blocks][H_kv][16][D] pool.
+// Element offset of tile (physical block, kv head) in a [blocks][H_kv][bs][D] pool.
 __device__ __forceinline__ size_t pa_tile_offset(int physical, int kv_head, int num_kv_heads,
-                                                 int head_dim) {
-  return (static_cast<size_t>(physical) * num_kv_heads + kv_head) * kBlockSize * head_dim;
+                                                 int head_dim, int bs) {
+  return (static_cast<size_t>(physical) * num_kv_heads + kv_head) * bs * head_dim;
 }
 
 __device__ __forceinline__ int pa_clamp_len(int len, int max_len) {

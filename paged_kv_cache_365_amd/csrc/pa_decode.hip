@@ -275,6 +275,11 @@ __device__ __forceinline__ float sum_over_q(float v) {
 struct Unit {
   int sibling, part, kv_head, seq;
 };
+
+// physical blocks of one 16-token step (b == a for 16-token blocks)
+struct Phys {
+  int a, b;
+};
 __device__ __forceinline__ Unit unit_of(int id, int total, int wgs, int parts, int kv_heads) {
   constexpr int kXcds = 8;
   int n = id;
@@ -297,7 +302,7 @@ __device__ __forceinline__ Unit unit_of(int id, int total, int wgs, int parts, i
   return u;
 }
 
-template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared>
+template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared, int kBS>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   // Sibling workgroups (kShared) read each tile through the XCD's L2 one after
   // another, so their loads must not carry the streaming hint.
@@ -330,8 +335,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
   const int t_lo = part * a.partition_tokens;
   const int t_hi = min(L, t_lo + a.partition_tokens);
-  const int blk_lo = t_lo / kBlockSize;
-  const int blk_hi = t_hi > t_lo ? (t_hi + kBlockSize - 1) / kBlockSize : blk_lo;
+  // 16-token steps of the partition (a step is one 16-token block or two
+  // 8-token blocks)
+  const int blk_lo = t_lo / kStep;
+  const int blk_hi = t_hi > t_lo ? (t_hi + kStep - 1) / kStep : blk_lo;
   // Query token i sees the tokens [0, L - T + 1 + i) (the draft is causal; one
   // query token sees the whole context).  Blocks that end past the smallest
   // limit of this workgroup's rows are masked row by row.
@@ -421,27 +428,56 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const char* __restrict__ kbase = static_cast<const char*>(a.k_pool);
   const char* __restrict__ vbase = static_cast<const char*>(a.v_pool);
 
-  // physical block of a (valid) logical block, read through the scalar cache
-  auto physical = [&](int jb) { return pa_physical_block(trow, jb, a.num_blocks); };
+  // Physical blocks of 16-token step jb, read through the scalar cache: one
+  // 16-token block, or two 8-token blocks (the second one repeats the first
+  // when the context ends inside the first: its tokens are masked anyway).
+  const int live_blocks = (L + kBS - 1) / kBS;
+  auto physical = [&](int jb) {
+    Phys p;
+    if constexpr (kBS == 16) {
+      p.a = p.b = pa_physical_block(trow, jb, a.num_blocks);
+    } else {
+      p.a = pa_physical_block(trow, 2 * jb, a.num_blocks);
+      p.b = 2 * jb + 1 < live_blocks ? pa_physical_block(trow, 2 * jb + 1, a.num_blocks) : p.a;
+    }
+    return p;
+  };
 
-  auto load = [&](int phys, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
-    const size_t tile = pa_tile_offset(phys, g, a.num_kv_heads, D);  // elements
-    const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile * M::kKBytes);
-    const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + tile * M::kVBytes);
+  auto load = [&](Phys ph, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
+    if constexpr (kBS == 16) {
+      const size_t tile = pa_tile_offset(ph.a, g, a.num_kv_heads, D, 16);  // elements
+      const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile * M::kKBytes);
+      const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + tile * M::kVBytes);
 #pragma unroll
-    for (int j = 0; j < kKLoads; ++j) kr[j] = load16<kStreamK>(kt + 64 * j + lane);
+      for (int j = 0; j < kKLoads; ++j) kr[j] = load16<kStreamK>(kt + 64 * j + lane);
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = load16<kStreamV>(vt + (16 * cb + r) * 4 + qg);
+      for (int cb = 0; cb < kColBlocks; ++cb)
+        vr[cb] = load16<kStreamV>(vt + (16 * cb + r) * 4 + qg);
+    } else {
+      // 8-token tiles: K token r of the step is token r % 8 of block r / 8 (the
+      // lane's chunk 4j + qg at [chunk][r % 8]: 512 contiguous bytes per half
+      // wave); V tokens 4qg .. 4qg+3 are tokens 4 (qg % 2) .. of block qg / 2.
+      const size_t ta = pa_tile_offset(ph.a, g, a.num_kv_heads, D, 8);
+      const size_t tb = pa_tile_offset(ph.b, g, a.num_kv_heads, D, 8);
+      const uint4* kt = reinterpret_cast<const uint4*>(kbase + (r < 8 ? ta : tb) * M::kKBytes);
+      const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + (qg < 2 ? ta : tb) * M::kVBytes);
+#pragma unroll
+      for (int j = 0; j < kKLoads; ++j)
+        kr[j] = load16<kStreamK>(kt + (4 * j + qg) * 8 + (r & 7));
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb)
+        vr[cb] = load16<kStreamV>(vt + (16 * cb + r) * 2 + (qg & 1));
+    }
   };
 
   auto consume = [&](int jb, const uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
-    const int tok0 = jb * kBlockSize + 4 * qg;  // first token of this lane's four
-    if ((jb + 1) * kBlockSize > t_hi) {          // V rows past the partition (wave-uniform test)
+    const int tok0 = jb * kStep + 4 * qg;  // first token of this lane's four
+    if ((jb + 1) * kStep > t_hi) {          // V rows past the partition (wave-uniform test)
       const int n = min(max(t_hi - tok0, 0), 4);
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) M::keep(vr[cb], n);
     }
-    const bool masked = (jb + 1) * kBlockSize > t_hi_min;  // wave-uniform
+    const bool masked = (jb + 1) * kStep > t_hi_min;  // wave-uniform
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -482,7 +518,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   uint4 kr[kDepth][kKLoads];
   VLoad vr[kDepth][kColBlocks];
   const int first = blk_lo + wave;
-  int next_phys = 0;
+  Phys next_phys{0, 0};
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d) {
     const int jb = first + d * kWaves;
@@ -574,18 +610,18 @@ int chunks_for(int rows) {
   return c < PA_MAX_CHUNKS ? c : PA_MAX_CHUNKS;
 }
 
-template <class M, class Tr, int D, int kChunks, bool kShared>
+template <class M, class Tr, int D, int kChunks, bool kShared, int kBS>
 hipError_t launch_cs(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   // Four chunks hold 64 rows of state per lane: only 4 waves per workgroup fit
   // them without spilling.
   if constexpr (kChunks < 4) {
     if (a.partition_tokens >= kWideTokens) {
-      hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kShared>), grid, dim3(8 * 64), 0,
+      hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kShared, kBS>), grid, dim3(8 * 64), 0,
                          stream, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kShared>), grid, dim3(4 * 64), 0,
+  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kShared, kBS>), grid, dim3(4 * 64), 0,
                      stream, a);
   return hipGetLastError();
 }
@@ -595,8 +631,12 @@ hipError_t launch_c(const DecodeArgs& a, hipStream_t stream) {
   const int rows = a.num_query_tokens * (a.num_q_heads / a.num_kv_heads);
   const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
   const dim3 grid(a.num_parts * a.num_kv_heads * wgs * a.num_seqs);
-  if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true>(a, grid, stream);
-  return launch_cs<M, Tr, D, kChunks, false>(a, grid, stream);
+  if (a.block_size == 8) {
+    if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true, 8>(a, grid, stream);
+    return launch_cs<M, Tr, D, kChunks, false, 8>(a, grid, stream);
+  }
+  if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true, 16>(a, grid, stream);
+  return launch_cs<M, Tr, D, kChunks, false, 16>(a, grid, stream);
 }
 
 template <class M, class Tr, int D>

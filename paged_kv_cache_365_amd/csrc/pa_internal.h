@@ -25,6 +25,7 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t num_blocks;
+  int32_t block_size;        // tokens per physical block: 16 or 8
   int32_t max_context_len;
   int32_t dtype;
   float scale;
@@ -58,8 +59,8 @@ hipError_t launch_fill(void* dst, size_t bytes16, uint32_t pattern, hipStream_t 
 
 hipError_t launch_write_kv(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                            const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                           int32_t num_kv_heads, int32_t row_bytes, int32_t elem_bytes,
-                           hipStream_t stream);
+                           int32_t block_size, int32_t num_kv_heads, int32_t row_bytes,
+                           int32_t elem_bytes, hipStream_t stream);
 
 struct BlockMoveArgs {
   const void* src_k;
@@ -81,11 +82,12 @@ hipError_t launch_block_move(const BlockMoveArgs& a, hipStream_t stream);
 
 hipError_t launch_write_kv_k8(void* k_pool, void* v_pool, const float* k_scale, const void* k_new,
                               const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
-                              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t dtype, hipStream_t stream);
+                              int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t dtype, hipStream_t stream);
 
 hipError_t launch_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
-                           int32_t num_blocks, int64_t* slot_ids, hipStream_t stream);
+                           int32_t num_blocks, int32_t block_size, int64_t* slot_ids,
+                           hipStream_t stream);
 
 }  // namespace pa

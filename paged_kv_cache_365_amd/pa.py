@@ -83,7 +83,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_reduce.restype = ctypes.c_int
     lib.pa_reduce.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_debug_slot_ids.restype = ctypes.c_int
-    lib.pa_debug_slot_ids.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
+    lib.pa_debug_slot_ids.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [desc, vp, vp, vp, i32, vp]
     lib.pa_gather_blocks.restype = ctypes.c_int
@@ -207,11 +207,11 @@ def pa_reduce(workspace, context_lens, num_seqs: int, num_q_heads: int, head_dim
 
 
 def pa_debug_slot_ids(block_tables, context_lens, max_context_len: int, num_blocks: int,
-                      slot_ids, stream=None) -> None:
+                      slot_ids, stream=None, block_size: int = BLOCK_SIZE) -> None:
     B = int(context_lens.shape[0])
     _check("pa_debug_slot_ids", load().pa_debug_slot_ids(
         _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
-        int(max_context_len), int(num_blocks), _ptr(slot_ids), _stream(stream)))
+        int(max_context_len), int(num_blocks), int(block_size), _ptr(slot_ids), _stream(stream)))
 
 
 def pa_copy_blocks(k_pool, v_pool, src_dst, stream=None) -> None:

@@ -56,11 +56,12 @@ def chunk_elems(dtype: str) -> int:
     return 16 // ELEM_BYTES[dtype]
 
 
-def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str):
+def pool_shapes(num_blocks: int, num_kv_heads: int, head_dim: int, dtype: str,
+                block_size: int = BLOCK_SIZE):
     """(K pool shape, V pool shape) of the library's layout."""
     x = chunk_elems(dtype)
-    return ((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x),
-            (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE))
+    return ((num_blocks, num_kv_heads, head_dim // x, block_size, x),
+            (num_blocks, num_kv_heads, head_dim, block_size))
 
 
 # --------------------------------------------------------------------------
@@ -146,6 +147,10 @@ class Workload:
         return int(self.block_tables.shape[1])
 
     @property
+    def block_size(self) -> int:
+        return int(self.k_pool.shape[3])
+
+    @property
     def max_context_len(self) -> int:
         return int(self.context_lens.max()) if self.context_lens.size else 0
 
@@ -166,7 +171,7 @@ class Workload:
         """K+V bytes of the distinct live token slots (shared prefix counted once)."""
         per_token = 2 * self.num_kv_heads * self.head_dim * ELEM_BYTES[self.dtype]
         lens = self.context_lens.astype(np.int64)
-        shared = self.prefix_blocks * BLOCK_SIZE
+        shared = self.prefix_blocks * self.block_size
         if shared and len(lens):
             return int(shared + (lens - shared).sum()) * per_token
         return int(lens.sum()) * per_token
@@ -179,7 +184,8 @@ class Workload:
         float32 channel scales are read too."""
         e = ELEM_BYTES[self.dtype]
         qo = 2 * query_tokens * self.num_seqs * self.num_q_heads * self.head_dim * e
-        live_entries = int(((self.context_lens.astype(np.int64) + BLOCK_SIZE - 1) // BLOCK_SIZE).sum())
+        bs = self.block_size
+        live_entries = int(((self.context_lens.astype(np.int64) + bs - 1) // bs).sum())
         if unique:
             kv = self.kv_bytes_unique()
         else:
@@ -205,8 +211,8 @@ def k8_inputs(w: "Workload", seed: int, outlier_columns: int = 0, outlier_gain: 
     the slots past each context in its last block hold -128.  Returns
     (k8_pool int8, k_scale float32)."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    NB, Hkv, d = w.num_blocks, w.num_kv_heads, w.head_dim
-    shape = (NB, Hkv, d // 16, BLOCK_SIZE, 16)
+    NB, Hkv, d, bs = w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size
+    shape = (NB, Hkv, d // 16, bs, 16)
     draws = normal(rng, shape, "f32", gain=K8_CODE_SPREAD)
     codes = np.clip(np.rint(draws), -127, 127).astype(np.int8)
     k_scale = np.full((Hkv, d), K8_BASE_SCALE, dtype=np.float32)
@@ -217,9 +223,9 @@ def k8_inputs(w: "Workload", seed: int, outlier_columns: int = 0, outlier_gain: 
         codes[w.free_blocks] = K8_POISON
     for s in range(w.num_seqs):
         L = int(w.context_lens[s])
-        o = L % BLOCK_SIZE
+        o = L % bs
         if L and o:
-            codes[w.block_tables[s, L // BLOCK_SIZE], :, :, o:, :] = K8_POISON
+            codes[w.block_tables[s, L // bs], :, :, o:, :] = K8_POISON
     return codes, k_scale
 
 
@@ -246,6 +252,7 @@ def build_workload(
     tail_fill: str = "nan",
     partition_size: int = 0,
     scale: float | None = None,
+    block_size: int = BLOCK_SIZE,
 ) -> Workload:
     """Draw one workload.
 
@@ -257,10 +264,11 @@ def build_workload(
     """
     lens = np.asarray(context_lens, dtype=np.int32)
     B = len(lens)
-    if prefix_tokens % BLOCK_SIZE:
+    bs = block_size
+    if prefix_tokens % bs:
         raise ValueError("shared prefix must be a whole number of blocks")
-    prefix_blocks = prefix_tokens // BLOCK_SIZE
-    need = [(int(L) + BLOCK_SIZE - 1) // BLOCK_SIZE for L in lens]
+    prefix_blocks = prefix_tokens // bs
+    need = [(int(L) + bs - 1) // bs for L in lens]
     if max_blocks_per_seq is None:
         max_blocks_per_seq = max(need) if need else 1
     max_blocks_per_seq = max(max_blocks_per_seq, 1)
@@ -283,7 +291,7 @@ def build_workload(
         cursor += n
     free = perm[used:]
 
-    kshape, vshape = pool_shapes(pool_blocks, num_kv_heads, head_dim, dtype)
+    kshape, vshape = pool_shapes(pool_blocks, num_kv_heads, head_dim, dtype, bs)
     x = chunk_elems(dtype)
     k_pool = normal(rng, kshape, dtype)
     v_pool = normal(rng, vshape, dtype)
@@ -293,7 +301,7 @@ def build_workload(
         cols = rng.choice(num_kv_heads * head_dim, size=k_outlier_columns, replace=False)
         for c in np.sort(cols):
             g, ch = divmod(int(c), head_dim)
-            k_pool[:, g, ch // x, :, ch % x] = normal(rng, (pool_blocks, BLOCK_SIZE), dtype,
+            k_pool[:, g, ch // x, :, ch % x] = normal(rng, (pool_blocks, bs), dtype,
                                                       gain=outlier_gain)
     q = normal(rng, (B, num_q_heads, head_dim), dtype)
 
@@ -303,12 +311,12 @@ def build_workload(
             v_pool[free] = nan_fill((len(free),) + vshape[1:], dtype)
         for s in range(B):
             L = int(lens[s])
-            o = L % BLOCK_SIZE
+            o = L % bs
             if L == 0 or o == 0:
                 continue
-            b = tables[s, L // BLOCK_SIZE]
-            kt = (num_kv_heads, head_dim // x, BLOCK_SIZE - o, x)
-            vt = (num_kv_heads, head_dim, BLOCK_SIZE - o)
+            b = tables[s, L // bs]
+            kt = (num_kv_heads, head_dim // x, bs - o, x)
+            vt = (num_kv_heads, head_dim, bs - o)
             if tail_fill == "nan":
                 k_pool[b, :, :, o:, :] = nan_fill(kt, dtype)
                 v_pool[b, :, :, o:] = nan_fill(vt, dtype)
@@ -339,40 +347,45 @@ CONFIG_NAMES = (
 
 
 def make_config(index: int, seed: int | None = None, *, poison: bool = True,
-                tail_fill: str = "nan") -> Workload:
-    """Workload ``index`` (0..4) drawn with ``seed`` (default 1000 + index)."""
+                tail_fill: str = "nan", block_size: int = BLOCK_SIZE) -> Workload:
+    """Workload ``index`` (0..4) drawn with ``seed`` (default 1000 + index).  With
+    ``block_size`` 8 the same shapes are cut into 8-token blocks (named with a
+    "-bs8" suffix); the table width doubles."""
     if seed is None:
         seed = 1000 + index
     rng = np.random.Generator(np.random.PCG64(seed))
-    name = CONFIG_NAMES[index]
-    kw = dict(poison=poison, tail_fill=tail_fill)
+    name = CONFIG_NAMES[index] + ("" if block_size == BLOCK_SIZE else f"-bs{block_size}")
+    per16 = BLOCK_SIZE // block_size   # table entries per 16 tokens
+    kw = dict(poison=poison, tail_fill=tail_fill, block_size=block_size)
     if index == 0:
         return build_workload(name, rng, dtype="f32", num_q_heads=4, num_kv_heads=4,
-                              head_dim=64, context_lens=[17, 40], pool_blocks=8, **kw)
+                              head_dim=64, context_lens=[17, 40], pool_blocks=8 * per16, **kw)
     if index == 1:
         lens = rng.integers(512, 4096, size=32, endpoint=True)
         return build_workload(name, rng, dtype="f16", num_q_heads=32, num_kv_heads=32,
-                              head_dim=128, context_lens=lens, max_blocks_per_seq=256, **kw)
+                              head_dim=128, context_lens=lens, max_blocks_per_seq=256 * per16,
+                              **kw)
     if index == 2:
         return build_workload(name, rng, dtype="bf16", num_q_heads=64, num_kv_heads=8,
-                              head_dim=128, context_lens=[4096] * 64, max_blocks_per_seq=256,
-                              k_outlier_columns=10, **kw)
+                              head_dim=128, context_lens=[4096] * 64,
+                              max_blocks_per_seq=256 * per16, k_outlier_columns=10, **kw)
     if index == 3:
         lens = 1024 + rng.integers(16, 1024, size=128, endpoint=True)
         return build_workload(name, rng, dtype="bf16", num_q_heads=32, num_kv_heads=8,
-                              head_dim=128, context_lens=lens, max_blocks_per_seq=128,
+                              head_dim=128, context_lens=lens, max_blocks_per_seq=128 * per16,
                               prefix_tokens=1024, **kw)
     if index == 4:
         return build_workload(name, rng, dtype="bf16", num_q_heads=64, num_kv_heads=8,
-                              head_dim=128, context_lens=[32768] * 4, max_blocks_per_seq=2048,
-                              partition_size=512, **kw)
+                              head_dim=128, context_lens=[32768] * 4,
+                              max_blocks_per_seq=2048 * per16, partition_size=512, **kw)
     raise IndexError(index)
 
 
 def make_random_case(seed: int, *, num_seqs: int, num_q_heads: int, num_kv_heads: int,
                      head_dim: int, dtype: str, lens=None, max_len: int = 80,
                      partition_size: int = 0, poison: bool = True, tail_fill: str = "nan",
-                     free_fraction: float = 0.25, prefix_tokens: int = 0) -> Workload:
+                     free_fraction: float = 0.25, prefix_tokens: int = 0,
+                     block_size: int = BLOCK_SIZE) -> Workload:
     """A small random case for parity sweeps (ragged lengths, several tiles)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     if lens is None:
@@ -380,4 +393,5 @@ def make_random_case(seed: int, *, num_seqs: int, num_q_heads: int, num_kv_heads
     return build_workload(f"random-{seed}", rng, dtype=dtype, num_q_heads=num_q_heads,
                           num_kv_heads=num_kv_heads, head_dim=head_dim, context_lens=lens,
                           free_fraction=free_fraction, poison=poison, tail_fill=tail_fill,
-                          partition_size=partition_size, prefix_tokens=prefix_tokens)
+                          partition_size=partition_size, prefix_tokens=prefix_tokens,
+                          block_size=block_size)

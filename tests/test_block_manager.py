@@ -33,8 +33,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 # an adapter giving the library the model's interface
 # --------------------------------------------------------------------------
 class Lib:
-    def __init__(self, num_blocks):
-        self.bm = BlockManager(num_blocks)
+    def __init__(self, num_blocks, block_size=BLOCK_SIZE):
+        self.bm = BlockManager(num_blocks, block_size)
         self.num_blocks = num_blocks
 
     def _call(self, fn, *a):
@@ -97,7 +97,8 @@ def model_append_step(m, seqs, token_ids=None):
 class Contents:
     """What each slot holds: the token prefix of the token written there."""
 
-    def __init__(self):
+    def __init__(self, bs=BLOCK_SIZE):
+        self.bs = bs
         self.slot = {}
         self.history = {}   # seq -> token ids it has written or shared
 
@@ -108,17 +109,19 @@ class Contents:
             self.slot[s] = tuple(h)
 
     def copy_block(self, src, dst):
-        for o in range(BLOCK_SIZE):
-            if src * BLOCK_SIZE + o in self.slot:
-                self.slot[dst * BLOCK_SIZE + o] = self.slot[src * BLOCK_SIZE + o]
+        bs = self.bs
+        for o in range(bs):
+            if src * bs + o in self.slot:
+                self.slot[dst * bs + o] = self.slot[src * bs + o]
             else:
-                self.slot.pop(dst * BLOCK_SIZE + o, None)
+                self.slot.pop(dst * bs + o, None)
 
     def check(self, seq, table, length):
         h = self.history[seq]
         assert len(h) == length
+        bs = self.bs
         for t in range(length):
-            s = table[t // BLOCK_SIZE] * BLOCK_SIZE + t % BLOCK_SIZE
+            s = table[t // bs] * bs + t % bs
             assert self.slot.get(s) == tuple(h[: t + 1]), (seq, t, s)
 
 
@@ -301,9 +304,9 @@ def test_exhaustion_changes_nothing(impl):
 # random traces: the model against the content simulation, the library
 # against the model
 # --------------------------------------------------------------------------
-def run_trace(seed, num_blocks, n_ops, impls, vocab=3):
+def run_trace(seed, num_blocks, n_ops, impls, vocab=3, bs=BLOCK_SIZE):
     rnd = random.Random(seed)
-    sims = [Contents() for _ in impls]
+    sims = [Contents(bs) for _ in impls]
     live, swapped, saved = [], [], {}
     next_id = 0
     sys_prompts = [[rnd.randrange(vocab) for _ in range(rnd.choice([16, 32, 40, 64]))]
@@ -381,7 +384,7 @@ def run_trace(seed, num_blocks, n_ops, impls, vocab=3):
         elif r < 0.9:
             seq = live.pop(rnd.randrange(len(live)))
             _, (table, L) = both(lambda m: m.swap_out(seq))
-            saved[seq] = [[sim.slot.get(b * BLOCK_SIZE + o) for b in table for o in range(BLOCK_SIZE)]
+            saved[seq] = [[sim.slot.get(b * bs + o) for b in table for o in range(bs)]
                           for sim in sims]
             swapped.append(seq)
         elif swapped:
@@ -391,7 +394,7 @@ def run_trace(seed, num_blocks, n_ops, impls, vocab=3):
                 swapped.pop(0)
                 for sim, vals in zip(sims, saved.pop(seq)):
                     for i, v in enumerate(vals):
-                        s = table[i // BLOCK_SIZE] * BLOCK_SIZE + i % BLOCK_SIZE
+                        s = table[i // bs] * bs + i % bs
                         if v is None:
                             sim.slot.pop(s, None)
                         else:
@@ -431,6 +434,28 @@ def test_model_random_trace_contents(seed):
 def test_library_matches_model(seed):
     nb = [24, 48, 96, 200][seed % 4]
     run_trace(100 + seed, num_blocks=nb, n_ops=400, impls=[BlockManagerModel(nb), Lib(nb)])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_eight_token_blocks_library_matches_model(seed):
+    """The 8-token block variant: the same operation-by-operation equality and
+    slot-content invariants, with blocks (and registered prefixes) of 8 tokens."""
+    nb = [16, 40, 96, 150][seed]
+    run_trace(300 + seed, num_blocks=nb, n_ops=400,
+              impls=[BlockManagerModel(nb, 8), Lib(nb, 8)], bs=8)
+
+
+def test_eight_token_blocks_basics():
+    m, lib = BlockManagerModel(20, 8), Lib(20, 8)
+    for impl in (m, lib):
+        impl.add_seq(0)
+        assert impl.append(0, 20, list(range(20)))[0][:9] == list(range(9))   # blocks 0, 1, 2
+        impl.add_seq(1)
+        assert impl.match_prefix(1, list(range(20))) == 16                    # two full blocks
+        assert impl.table(1) == [0, 1]
+    with pytest.raises(pa.PAError) as e:
+        BlockManager(8, 12)
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED
 
 
 def test_library_errors():

@@ -89,11 +89,11 @@ def test_gather_scatter_bit_exact(dtype, d, hkv):
 # the serving trace
 # ---------------------------------------------------------------------------
 class Serving:
-    def __init__(self, seed, num_blocks, hkv, hq, d, dtype):
+    def __init__(self, seed, num_blocks, hkv, hq, d, dtype, block_size=16):
         self.rnd = random.Random(seed)
         self.nb, self.hkv, self.hq, self.d, self.dtype = num_blocks, hkv, hq, d, dtype
-        self.bm = BlockManager(num_blocks)
-        ks, vs = wl.pool_shapes(num_blocks, hkv, d, dtype)
+        self.bm = BlockManager(num_blocks, block_size)
+        ks, vs = wl.pool_shapes(num_blocks, hkv, d, dtype, block_size)
         self.kp = torch.empty(ks, dtype=TORCH_DTYPE[dtype], device=DEV)
         self.vp = torch.empty(vs, dtype=TORCH_DTYPE[dtype], device=DEV)
         pa.pa_init_pool(self.kp, self.vp, 1)     # NaN: a slot never written must never be read
@@ -218,10 +218,12 @@ class Serving:
             assert np.isfinite(got[i]).all() and err <= TOL[self.dtype], (s, err)
 
 
-@pytest.mark.parametrize("seed,dtype,hkv,hq,d", [(0, "bf16", 2, 16, 128), (1, "f32", 2, 4, 64),
-                                                 (2, "f16", 1, 8, 128)])
-def test_serving_trace(seed, dtype, hkv, hq, d):
-    srv = Serving(seed, num_blocks=80, hkv=hkv, hq=hq, d=d, dtype=dtype)
+@pytest.mark.parametrize("seed,dtype,hkv,hq,d,bs", [(0, "bf16", 2, 16, 128, 16),
+                                                    (1, "f32", 2, 4, 64, 16),
+                                                    (2, "f16", 1, 8, 128, 16),
+                                                    (3, "bf16", 2, 16, 128, 8)])
+def test_serving_trace(seed, dtype, hkv, hq, d, bs):
+    srv = Serving(seed, num_blocks=80 * 16 // bs, hkv=hkv, hq=hq, d=d, dtype=dtype, block_size=bs)
     rnd = random.Random(1000 + seed)
     sys_prompts = [[rnd.randrange(4) for _ in range(n)] for n in (32, 48, 70)]
     live, swapped = [], []

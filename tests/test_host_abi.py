@@ -74,7 +74,8 @@ def _decode(lib, desc=None, q=FAKE, kp=FAKE, vp=FAKE, tables=FAKE, mbs=4, lens=F
     (dict(maxlen=65), pa.PA_ERR_INVALID_ARG),     # > 16 * max_blocks_per_seq
     (dict(P=24), pa.PA_ERR_INVALID_ARG),          # not a multiple of 16
     (dict(P=-16), pa.PA_ERR_INVALID_ARG),
-    (dict(desc=_desc(bs=8)), pa.PA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(bs=12)), pa.PA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(bs=8), maxlen=33), pa.PA_ERR_INVALID_ARG),   # > 8 * max_blocks_per_seq
     (dict(desc=_desc(d=96)), pa.PA_ERR_UNSUPPORTED),
     (dict(desc=_desc(dtype=7)), pa.PA_ERR_UNSUPPORTED),
     (dict(desc=_desc(nb=0)), pa.PA_ERR_INVALID_ARG),
@@ -107,10 +108,12 @@ def test_reduce_and_other_calls_reject_bad_arguments(lib):
     assert w(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, 3, None) == pa.PA_ERR_INVALID_ARG
     assert w(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE + 4, 3, None) == pa.PA_ERR_MISALIGNED
     s = lib.pa_debug_slot_ids
-    assert s(FAKE, 4, FAKE, 2, 65, 8, FAKE, None) == pa.PA_ERR_INVALID_ARG
-    assert s(FAKE, 4, FAKE, 2, 40, 0, FAKE, None) == pa.PA_ERR_INVALID_ARG
-    assert s(FAKE, 4, FAKE, 2, 40, 8, FAKE + 4, None) == pa.PA_ERR_MISALIGNED
-    assert s(FAKE, 4, FAKE, 2, 0, 8, FAKE, None) == pa.PA_OK   # empty: nothing launched
+    assert s(FAKE, 4, FAKE, 2, 65, 8, 16, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert s(FAKE, 4, FAKE, 2, 33, 8, 8, FAKE, None) == pa.PA_ERR_INVALID_ARG   # > 8 * 4
+    assert s(FAKE, 4, FAKE, 2, 40, 0, 16, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert s(FAKE, 4, FAKE, 2, 40, 8, 12, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert s(FAKE, 4, FAKE, 2, 40, 8, 16, FAKE + 4, None) == pa.PA_ERR_MISALIGNED
+    assert s(FAKE, 4, FAKE, 2, 0, 8, 16, FAKE, None) == pa.PA_OK   # empty: nothing launched
 
 
 def test_binding_raises_on_error_status(lib):
@@ -126,7 +129,7 @@ def test_block_moves_reject_bad_arguments(lib):
     assert c(ctypes.byref(d), FAKE, FAKE, FAKE, -1, None) == pa.PA_ERR_INVALID_ARG
     assert c(ctypes.byref(d), FAKE, FAKE, None, 2, None) == pa.PA_ERR_INVALID_ARG
     assert c(ctypes.byref(d), FAKE + 8, FAKE, FAKE, 2, None) == pa.PA_ERR_MISALIGNED
-    assert c(ctypes.byref(_desc(bs=8)), FAKE, FAKE, FAKE, 2, None) == pa.PA_ERR_UNSUPPORTED
+    assert c(ctypes.byref(_desc(bs=12)), FAKE, FAKE, FAKE, 2, None) == pa.PA_ERR_UNSUPPORTED
     assert g(ctypes.byref(d), FAKE, FAKE, FAKE, 0, FAKE, FAKE, None) == pa.PA_OK
     assert g(ctypes.byref(d), FAKE, FAKE, FAKE, 2, None, FAKE, None) == pa.PA_ERR_INVALID_ARG
     assert g(ctypes.byref(d), FAKE, FAKE, FAKE, 2, FAKE + 4, FAKE, None) == pa.PA_ERR_MISALIGNED

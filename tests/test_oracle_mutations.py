@@ -19,8 +19,8 @@ ORACLE = os.path.join(ROOT, "oracle", "paged_attention.py")
 MUTATIONS = {
     "gqa_mod": ("return h // group", "return h % group"),
     "no_scale": ("x = scale * (K @ q_vec)", "x = (K @ q_vec)"),
-    "offset_shift": ("offset = t % BLOCK_SIZE\n    n_chunks", "offset = (t + 1) % BLOCK_SIZE\n    n_chunks"),
-    "v_offset_shift": ("offset = t % BLOCK_SIZE\n    d = ", "offset = (t + 1) % BLOCK_SIZE\n    d = "),
+    "offset_shift": ("offset = t % bs\n    n_chunks", "offset = (t + 1) % bs\n    n_chunks"),
+    "v_offset_shift": ("offset = t % bs\n    d = ", "offset = (t + 1) % bs\n    d = "),
     "k_chunk_swap": ("rows[:, c, :] = k_pool[physical, kv_head, c, offset, :]",
                      "rows[:, c, :] = k_pool[physical, kv_head, c ^ 1, offset, :]"),
     "v_col_swap": ("rows[:, c] = v_pool[physical, kv_head, c, offset]",
@@ -29,7 +29,7 @@ MUTATIONS = {
     "merge_unnorm": ("weights = np.exp(lse - total)", "weights = np.exp(lse - M)"),
     "bf16_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "lse_wrong": ("return out, m + np.log(z)", "return out, np.log(z)"),
-    "slot_wrong": ("return physical * BLOCK_SIZE + offset", "return physical * BLOCK_SIZE + offset + 1"),
+    "slot_wrong": ("return physical * block_size + offset", "return physical * block_size + offset + 1"),
     "write_swap": ("k_out[b, g, c // x, o, c % x] = k_new[i, g, c]",
                    "k_out[b, g, c // x, o, c % x] = v_new[i, g, c]"),
     "partition_hi": ("lo, hi = p * partition_size, min(L, (p + 1) * partition_size)",
@@ -70,12 +70,12 @@ BM_MUTATIONS = {
     "cow_no_decref": [("                self.ref[src] -= 1              # still referenced by another table\n", "")],
     "release_forward": [("for b in reversed(self.tables.pop(seq)):", "for b in self.tables.pop(seq):")],
     "evict_newest": [("self.cached.popitem(last=False)", "self.cached.popitem(last=True)")],
-    "match_whole_prompt": [("n_blocks = max(len(prompt) - 1, 0) // BLOCK_SIZE",
-                            "n_blocks = len(prompt) // BLOCK_SIZE")],
-    "key_without_prefix": [("key = tuple(prompt[: (i + 1) * BLOCK_SIZE])",
-                            "key = tuple(prompt[i * BLOCK_SIZE:(i + 1) * BLOCK_SIZE])"),
+    "match_whole_prompt": [("n_blocks = max(len(prompt) - 1, 0) // self.bs",
+                            "n_blocks = len(prompt) // self.bs")],
+    "key_without_prefix": [("key = tuple(prompt[: (i + 1) * self.bs])",
+                            "key = tuple(prompt[i * self.bs:(i + 1) * self.bs])"),
                            ("                    key = tuple(toks)\n",
-                            "                    key = tuple(toks[-BLOCK_SIZE:])\n")],
+                            "                    key = tuple(toks[-self.bs:])\n")],
     "cached_to_stack": [("            if b in self.key_of:\n                self.cached[b] = True",
                          "            if False:\n                self.cached[b] = True")],
     "stack_fifo": [("return self.free.pop()", "return self.free.pop(0)")],

@@ -41,32 +41,33 @@ def put_token(kp, vp, blk, off, k_row, v_row):
             vp[blk, g, c, off] = v_row[g, c]
 
 
-def empty_pools(nb, Hkv, d, dtype, fill=0):
+def empty_pools(nb, Hkv, d, dtype, fill=0, bs=BS):
     x = 16 // np.dtype(dtype).itemsize
-    return (np.full((nb, Hkv, d // x, BS, x), fill, dtype=dtype),
-            np.full((nb, Hkv, d, BS), fill, dtype=dtype))
+    return (np.full((nb, Hkv, d // x, bs, x), fill, dtype=dtype),
+            np.full((nb, Hkv, d, bs), fill, dtype=dtype))
 
 
-def scatter_to_pool(K, V, lens, rng, extra_blocks=3):
-    """Contiguous K, V [B][Lmax][H_kv][d] -> a randomly permuted paged pool.
+def scatter_to_pool(K, V, lens, rng, extra_blocks=3, bs=BS):
+    """Contiguous K, V [B][Lmax][H_kv][d] -> a randomly permuted paged pool of
+    bs-token blocks.
 
     Written here with its own index arithmetic so the paged oracle's gather is
     checked against something it does not share.
     """
     B, Lmax, Hkv, d = K.shape
-    need = [-(-int(L) // BS) for L in lens]
+    need = [-(-int(L) // bs) for L in lens]
     nb = sum(need) + extra_blocks
     perm = rng.permutation(nb)
     width = max(max(need), 1)
     tables = np.full((B, width), -1, dtype=np.int32)
-    kp, vp = empty_pools(nb, Hkv, d, K.dtype)
+    kp, vp = empty_pools(nb, Hkv, d, K.dtype, bs=bs)
     c = 0
     for s in range(B):
         for j in range(need[s]):
             tables[s, j] = perm[c]
             c += 1
         for t in range(int(lens[s])):
-            put_token(kp, vp, tables[s, t // BS], t % BS, K[s, t], V[s, t])
+            put_token(kp, vp, tables[s, t // bs], t % bs, K[s, t], V[s, t])
     return kp, vp, tables
 
 
@@ -603,6 +604,55 @@ def test_verify_partials_merge_to_verify(P):
     merged = oracle.merge_partials(o, lse).reshape(3, T, Hkv * G, d)
     want = oracle.paged_verify(Q, kp, vp, tab, np.array(lens), 0.125, "f32")
     np.testing.assert_allclose(merged, want, rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# 8-token blocks ([P3] §2.2: the block size falls back to 8 for 70B models)
+# ---------------------------------------------------------------------------
+def test_slots_with_8_token_blocks():
+    """The page's table [#7, #2, #11] with 8-token blocks: tokens 0-7, 8-15 and
+    16-23 land in physical blocks 7, 2 and 11 (slots 56-63, 16-23, 88-95)."""
+    row = np.array([7, 2, 11], np.int32)
+    got = [oracle.slot_of(row, t, 8) for t in range(24)]
+    assert got == list(range(56, 64)) + list(range(16, 24)) + list(range(88, 96))
+    ids = oracle.slot_ids(row[None], np.array([20]), 24, 8)[0]
+    assert list(ids[:20]) == got[:20] and (ids[20:] == -1).all()
+    assert oracle.tile_byte_offset(2, 1, 4, 128, 2, 8) == (2 * 4 + 1) * 8 * 128 * 2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_8_token_blocks_give_the_16_token_result(dtype):
+    """The same context cut into 8- or 16-token blocks is the same attention:
+    bit-identical oracle outputs, and equal to the dense brute force."""
+    rng = np.random.default_rng(78)
+    B, Hkv, G, d = 3, 2, 4, 64
+    lens = [5, 24, 61]
+    K = wl.normal(rng, (B, max(lens), Hkv, d), dtype)
+    V = wl.normal(rng, (B, max(lens), Hkv, d), dtype)
+    q = wl.normal(rng, (B, Hkv * G, d), dtype)
+    outs = []
+    for bs in (16, 8):
+        kp, vp, tab = scatter_to_pool(K, V, lens, rng, bs=bs)
+        outs.append(oracle.paged_decode(q, kp, vp, tab, np.array(lens), 0.125, dtype))
+    assert np.array_equal(outs[0], outs[1])
+    for s in range(B):
+        want = oracle.dense_attention(oracle.widen(q[s], dtype), oracle.widen(K[s, :lens[s]], dtype),
+                                      oracle.widen(V[s, :lens[s]], dtype), 0.125)
+        np.testing.assert_allclose(outs[1][s], want, rtol=0, atol=1e-12)
+
+
+def test_write_kv_with_8_token_blocks():
+    rng = np.random.default_rng(79)
+    nb, Hkv, d, T = 6, 2, 64, 20
+    ks, vs = wl.pool_shapes(nb, Hkv, d, "bf16", 8)
+    kp, vp = wl.normal(rng, ks, "bf16"), wl.normal(rng, vs, "bf16")
+    kn, vn = wl.normal(rng, (T, Hkv, d), "bf16"), wl.normal(rng, (T, Hkv, d), "bf16")
+    slots = rng.choice(nb * 8, size=T, replace=False).astype(np.int64)
+    k2, v2 = oracle.write_kv(kp, vp, kn, vn, slots)
+    ke, ve = kp.copy(), vp.copy()
+    for i, sl in enumerate(slots):
+        put_token(ke, ve, sl // 8, sl % 8, kn[i], vn[i])
+    assert np.array_equal(k2, ke) and np.array_equal(v2, ve)
 
 
 # ---------------------------------------------------------------------------
