@@ -302,7 +302,8 @@ __device__ __forceinline__ Unit unit_of(int id, int total, int wgs, int parts, i
   return u;
 }
 
-template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared, int kBS>
+template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared, int kBS,
+          bool kWavePart>
 __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   // Sibling workgroups (kShared) read each tile through the XCD's L2 one after
   // another, so their loads must not carry the streaming hint.
@@ -312,11 +313,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   constexpr int kQOps = kKLoads * M::kQOps;      // B operands of the logits per row
   constexpr int kColBlocks = D / 16;           // P.V output blocks of 16 columns
   constexpr int kPad = 4;                      // LDS row padding (floats)
+  // kWavePart (split mode): each wave owns one whole partition and writes its
+  // partial itself, so a workgroup covers kWaves consecutive partitions with
+  // no merge through LDS; otherwise the waves share one partition's blocks.
+  constexpr int kStride = kWavePart ? 1 : kWaves;  // logical-step stride of a wave
   using VLoad = typename M::VLoad;
-
-  __shared__ float sm_o[kWaves][16][D + kPad];
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
 
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
@@ -326,11 +327,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int rows = T * group;  // (query token, query head) rows that read KV head g
   const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
-  const Unit u = unit_of(blockIdx.x, gridDim.x, wgs, a.num_parts, a.num_kv_heads);
-  const int part = u.part;
+  const int part_units = kWavePart ? (a.num_parts + kWaves - 1) / kWaves : a.num_parts;
+  const Unit u = unit_of(blockIdx.x, gridDim.x, wgs, part_units, a.num_kv_heads);
+  const int part = kWavePart ? u.part * kWaves + wave : u.part;
   const int g = u.kv_head;
   const int row0 = u.sibling * (16 * kChunks);
   const int s = u.seq;
+  if (kWavePart && part >= a.num_parts) return;  // a wave past the last partition (no barriers)
 
   const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
   const int t_lo = part * a.partition_tokens;
@@ -511,43 +514,68 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // A ring of kDepth register sets: the wave's i-th block (logical block
-  // blk_lo + wave + i * kWaves) is consumed while blocks i+1 .. i+kDepth-1 are
-  // in flight.  The physical id of the block to load next is read one
-  // iteration before its tile loads are issued.
+  // A ring of kDepth register sets: the wave's i-th step (blk_lo + wave + i *
+  // kWaves when the waves share a partition, blk_lo + i when the wave owns it)
+  // is consumed while steps i+1 .. i+kDepth-1 are in flight.  The physical id
+  // of the step to load next is read one iteration before its tile loads are
+  // issued.
   uint4 kr[kDepth][kKLoads];
   VLoad vr[kDepth][kColBlocks];
-  const int first = blk_lo + wave;
+  const int first = blk_lo + (kWavePart ? 0 : wave);
   Phys next_phys{0, 0};
 #pragma unroll
   for (int d = 0; d < kDepth - 1; ++d) {
-    const int jb = first + d * kWaves;
+    const int jb = first + d * kStride;
     if (jb < blk_hi) load(physical(jb), kr[d], vr[d]);
   }
   {
-    const int jb = first + (kDepth - 1) * kWaves;
+    const int jb = first + (kDepth - 1) * kStride;
     if (jb < blk_hi) next_phys = physical(jb);
   }
   for (int base = 0;; base += kDepth) {
     bool done = false;
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      const int jb = first + (base + u) * kWaves;
+      const int jb = first + (base + u) * kStride;
       if (jb >= blk_hi) {
         done = true;
         break;
       }
-      const int jn = jb + (kDepth - 1) * kWaves;  // the block entering the ring
+      const int jn = jb + (kDepth - 1) * kStride;  // the step entering the ring
       if (jn < blk_hi) {
         load(next_phys, kr[(u + kDepth - 1) % kDepth], vr[(u + kDepth - 1) % kDepth]);
-        if (jn + kWaves < blk_hi) next_phys = physical(jn + kWaves);
+        if (jn + kStride < blk_hi) next_phys = physical(jn + kStride);
       }
       consume(jb, kr[u], vr[u]);
     }
     if (done) break;
   }
 
+  if constexpr (kWavePart) {
+    // this wave's partition: normalise in registers and write the partial
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int rho = row0 + 16 * c + r;
+      const float ls = sum_over_q(lsum[c]);  // all lanes take part
+      if (rho >= rows) continue;
+      const bool seen = m[c] != -INFINITY;
+      const float inv = seen ? 1.f / ls : 0.f;
+      const size_t row = (static_cast<size_t>(s) * T + rho / group) * a.num_q_heads +
+                         g * group + rho % group;
+      float* op = a.o_part + (row * a.num_parts + part) * D + 4 * qg;
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb)
+        *reinterpret_cast<f32x4*>(op + 16 * cb) = acc[c][cb] * inv;
+      if (qg == 0)
+        a.lse_part[row * a.num_parts + part] = seen ? (m[c] + __log2f(ls)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
+
   // merge the waves through LDS, one chunk of 16 rows at a time, and write
+  __shared__ float sm_o[kWaves][16][D + kPad];
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int nh = min(16, rows - (row0 + 16 * c));  // live rows of this chunk
@@ -598,6 +626,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 // evenly); shorter ones get 4.
 constexpr int kWideTokens = 4096;
 
+// One wave per partition needs at least this many partitions per sequence and
+// this many workgroups.
+constexpr int kWavePartMin = 8;
+constexpr unsigned kWavePartUnits = 256;
+
 // Row chunks per workgroup (at most PA_MAX_CHUNKS; two measured best on
 // MI355X: four chunks hold too much state per lane to keep enough waves
 // resident): the rows of one KV head in as few workgroups as allowed; when they
@@ -611,18 +644,30 @@ int chunks_for(int rows) {
 }
 
 template <class M, class Tr, int D, int kChunks, bool kShared, int kBS>
-hipError_t launch_cs(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+hipError_t launch_cs(const DecodeArgs& a, int wgs, hipStream_t stream) {
+  const unsigned units = a.num_kv_heads * wgs * a.num_seqs;
+  // Split mode over many partitions: one wave per partition, four partitions
+  // per workgroup, when that still gives every wave a partition and the chip
+  // enough workgroups (measured on the 32K batch: 512-token partitions 93.1 ->
+  // 85.7 us; with two partitions per sequence half the waves would idle).
+  const unsigned groups = (a.num_parts + 3) / 4;
+  if (a.write_partials && a.num_parts >= kWavePartMin && units * groups >= kWavePartUnits) {
+    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kShared, kBS, true>),
+                       dim3(units * groups), dim3(4 * 64), 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(units * a.num_parts);
   // Four chunks hold 64 rows of state per lane: only 4 waves per workgroup fit
   // them without spilling.
   if constexpr (kChunks < 4) {
     if (a.partition_tokens >= kWideTokens) {
-      hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kShared, kBS>), grid, dim3(8 * 64), 0,
-                         stream, a);
+      hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kShared, kBS, false>), grid,
+                         dim3(8 * 64), 0, stream, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kShared, kBS>), grid, dim3(4 * 64), 0,
-                     stream, a);
+  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kShared, kBS, false>), grid,
+                     dim3(4 * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -630,13 +675,12 @@ template <class M, class Tr, int D, int kChunks>
 hipError_t launch_c(const DecodeArgs& a, hipStream_t stream) {
   const int rows = a.num_query_tokens * (a.num_q_heads / a.num_kv_heads);
   const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
-  const dim3 grid(a.num_parts * a.num_kv_heads * wgs * a.num_seqs);
   if (a.block_size == 8) {
-    if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true, 8>(a, grid, stream);
-    return launch_cs<M, Tr, D, kChunks, false, 8>(a, grid, stream);
+    if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true, 8>(a, wgs, stream);
+    return launch_cs<M, Tr, D, kChunks, false, 8>(a, wgs, stream);
   }
-  if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true, 16>(a, grid, stream);
-  return launch_cs<M, Tr, D, kChunks, false, 16>(a, grid, stream);
+  if (wgs > 1) return launch_cs<M, Tr, D, kChunks, true, 16>(a, wgs, stream);
+  return launch_cs<M, Tr, D, kChunks, false, 16>(a, wgs, stream);
 }
 
 template <class M, class Tr, int D>

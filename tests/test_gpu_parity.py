@@ -291,3 +291,37 @@ def test_uniform_v_and_poisoned_slots():
     want = oracle.widen(c, "bf16")
     for h in range(8):
         assert np.abs(out[:, h] - want[h // 4]).max() <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# split mode with one wave per partition (many partitions per sequence and
+# enough workgroups: the 32K-style launch), against the oracle in full
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,hq,hkv,T,P,bs", [("bf16", 64, 8, 1, 32, 16), ("f16", 32, 8, 2, 48, 16),
+                                                 ("bf16", 64, 8, 1, 32, 8), ("f32", 16, 8, 1, 16, 16)])
+def test_split_one_wave_per_partition(dtype, hq, hkv, T, P, bs):
+    lens = [300, 301, 17, 512, 420, 64, 333, 600, 1, 288, 511, 450, 77, 390, 600, 256]
+    w = wl.make_random_case(880, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=128 if dtype != "f32" else 64, dtype=dtype, lens=lens,
+                            block_size=bs)
+    n_parts = oracle.num_partitions(w.max_context_len, P)
+    assert n_parts >= 8 and len(lens) * hkv * -(-n_parts // 4) >= 256   # the launch this covers
+    dw = upload(w, DEV)
+    q = wl.normal(np.random.default_rng(881), (len(lens), T, hq, w.head_dim), dtype)
+    n = pa.pa_decode_workspace_bytes(len(lens), T * hq, w.head_dim, w.max_context_len, P)
+    ws = torch.empty(n // 4, dtype=torch.float32, device=DEV)
+    out = pa.verify_attention(to_torch(q, dtype, DEV), dw.k_pool, dw.v_pool, dw.block_tables,
+                              dw.context_lens, w.max_context_len, w.scale, partition_size=P,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.paged_verify(q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                               dtype)
+    assert_close(widen_f32(out), want, TOL[dtype], f"{dtype} P{P} T{T} bs{bs}")
+    o_p, lse_p = split_workspace(ws, len(lens), T * hq, w.head_dim, n_parts)
+    wo, wlse = oracle.paged_verify_partials(q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                                            w.scale, dtype, P, w.max_context_len)
+    live = np.isfinite(wlse)
+    assert np.array_equal(np.isfinite(lse_p), live), "empty partitions must be -inf"
+    assert np.abs(lse_p[live] - wlse[live]).max(initial=0) <= LSE_TOL[dtype]
+    assert_close(o_p[live], wo[live], TOL[dtype], "partials")
+    assert not o_p[~live].any()
