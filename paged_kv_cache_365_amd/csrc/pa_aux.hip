@@ -16,7 +16,8 @@ namespace {
 //   1. weights: thread p < live partitions computes exp(lse_p - M) into LDS
 //      (M and the sum by a fixed-order block reduction);
 //   2. thread t owns 4 columns (t % (D/4)) and every G-th partition starting
-//      at t / (D/4), with G = 256 / (D/4) partition groups, float4 loads;
+//      at t / (D/4), with G = 256 / (D/4) partition groups, float4 loads (the
+//      first eight of them issued before step 1, since they need no weight);
 //   3. the G group sums are added in group order through LDS.
 // Every sum has a fixed order, so the result is bit-reproducible.
 // ---------------------------------------------------------------------------
@@ -36,6 +37,7 @@ template <class Tr, int D>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   constexpr int kCols4 = D / 4;                       // float4 column groups
   constexpr int kGroups = kReduceThreads / kCols4;    // partition groups
+  constexpr int kPre = 8;                             // partials loaded before the weights
   extern __shared__ float sm_w[];                     // [num_parts] weights
   __shared__ float sm_red[4];
   __shared__ float4 sm_acc[kGroups][kCols4];
@@ -43,9 +45,21 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int t = threadIdx.x;
+  const size_t row = static_cast<size_t>(s) * a.num_q_heads + h;
+  const int c4 = t % kCols4;
+  const int grp = t / kCols4;
+  const float4* op = reinterpret_cast<const float4*>(a.o_part + row * a.num_parts * D) + c4;
+  // The first kPre partials of this thread do not depend on the weights (every
+  // partition of the workspace was written, empty ones as zeros): issue their
+  // loads first so they overlap the lse loads and the max reduction.
+  float4 pre[kPre];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int p = grp + i * kGroups;
+    pre[i] = p < a.num_parts ? op[static_cast<size_t>(p) * kCols4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
   const int nv = (L + a.partition_tokens - 1) / a.partition_tokens;  // live partitions
-  const size_t row = static_cast<size_t>(s) * a.num_q_heads + h;
   const float* lse = a.lse_part + row * a.num_parts;
 
   float mx = -INFINITY;
@@ -58,11 +72,19 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
   for (int p = t; p < nv; p += kReduceThreads) sm_w[p] = __expf(lse[p] - M);
   __syncthreads();
 
-  const int c4 = t % kCols4;
-  const int grp = t / kCols4;
-  const float4* op = reinterpret_cast<const float4*>(a.o_part + row * a.num_parts * D) + c4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p = grp; p < nv; p += kGroups) {
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) {
+    const int p = grp + i * kGroups;
+    if (p < nv) {
+      const float w = sm_w[p];
+      acc.x = fmaf(w, pre[i].x, acc.x);
+      acc.y = fmaf(w, pre[i].y, acc.y);
+      acc.z = fmaf(w, pre[i].z, acc.z);
+      acc.w = fmaf(w, pre[i].w, acc.w);
+    }
+  }
+  for (int p = grp + kPre * kGroups; p < nv; p += kGroups) {
     const float w = sm_w[p];
     const float4 v = op[static_cast<size_t>(p) * kCols4];
     acc.x = fmaf(w, v.x, acc.x);

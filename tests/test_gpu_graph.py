@@ -1,0 +1,103 @@
+"""GPU: the library under HIP-graph capture and on concurrent streams.
+
+Every entry point is asynchronous, allocates nothing, synchronises nothing and
+records no memset, so a decode step (KV append, split decode, log-sum-exp
+merge) can be captured once and replayed.  Each replay here is separated by
+the test's own eager work and synchronisations, gets new inputs written into
+the captured buffers, and must match the eager result bit for bit.  Two
+independent decodes on two streams must also match their single-stream
+results bit for bit (the library keeps no state between calls).
+"""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_365_amd import pa
+from paged_kv_cache_365_amd import workloads as wl
+from paged_kv_cache_365_amd.device import to_torch, upload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pa.load()
+
+
+def test_decode_step_graph_replays_match_eager():
+    dtype, P = "bf16", 32
+    lens = [40, 130, 257, 16]
+    w = wl.make_random_case(990, num_seqs=4, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                            dtype=dtype, lens=lens)
+    d = upload(w, DEV)
+    B, Hq, D = d.q.shape
+    rng = np.random.default_rng(991)
+    # static buffers the graph reads: q, one new token's K/V per sequence, its slot
+    q = torch.empty_like(d.q)
+    k_new = torch.empty((B, 2, D), dtype=d.q.dtype, device=DEV)
+    v_new = torch.empty_like(k_new)
+    slots = torch.tensor([int(w.block_tables[s, (L - 1) // 16]) * 16 + (L - 1) % 16
+                          for s, L in enumerate(lens)], dtype=torch.int64, device=DEV)
+    out = torch.empty_like(q)
+    n = pa.pa_decode_workspace_bytes(B, Hq, D, w.max_context_len, P)
+    ws = torch.empty(n // 4, dtype=torch.float32, device=DEV)
+
+    def fill_inputs():
+        q.copy_(to_torch(wl.normal(rng, (B, Hq, D), dtype), dtype, DEV))
+        k_new.copy_(to_torch(wl.normal(rng, (B, 2, D), dtype), dtype, DEV))
+        v_new.copy_(to_torch(wl.normal(rng, (B, 2, D), dtype), dtype, DEV))
+
+    def step(stream):
+        pa.pa_write_kv(d.k_pool, d.v_pool, k_new, v_new, slots, stream)
+        pa.pa_decode(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens, w.max_context_len,
+                     w.scale, P, ws, None, stream)
+        pa.pa_reduce(ws, d.context_lens, B, Hq, D, w.max_context_len, P, out, stream)
+
+    fill_inputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)                 # warm up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        fill_inputs()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        junk = torch.randn(1 << 20, device=DEV).sum()     # eager work between replays
+        step(torch.cuda.current_stream())                 # the same step, eagerly
+        torch.cuda.synchronize()
+        assert torch.equal(got, out), f"replay {rep} differs from the eager step"
+        del junk
+
+
+def test_two_streams_match_single_stream():
+    ws_ = []
+    cases = []
+    for i, (hq, hkv) in enumerate([(64, 8), (16, 16)]):
+        w = wl.make_random_case(995 + i, num_seqs=6, num_q_heads=hq, num_kv_heads=hkv,
+                                head_dim=128, dtype="bf16", max_len=900)
+        cases.append((w, upload(w, DEV)))
+    ref = []
+    for w, d in cases:
+        ref.append(pa.paged_attention(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                                      w.max_context_len, w.scale, partition_size=64))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(d.q) for _, d in cases]
+    for _ in range(3):
+        for (w, d), st, o in zip(cases, streams, outs):
+            ws_.append(pa.workspace_for(d.q, d.k_pool, w.max_context_len, 64))
+            pa.paged_attention(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                               w.max_context_len, w.scale, partition_size=64, workspace=ws_[-1],
+                               out=o, stream=st)
+        torch.cuda.synchronize()
+        for r, o in zip(ref, outs):
+            assert torch.equal(r, o)
