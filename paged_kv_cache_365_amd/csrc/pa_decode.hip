@@ -11,17 +11,21 @@
 // read the tiles through that XCD's L2 (see unit_of).
 //
 // Work unit.  A workgroup of kWaves wavefronts owns (sequence s, KV head g, up
-// to 16 * kChunks of g's rows, partition p).  The partition's 16-token blocks
-// are dealt round-robin to the waves; every wave streams its blocks through
-// registers, keeping the next block's K and V in flight while the current one
+// to 16 * kChunks of g's rows, partition p).  The partition's 16-token steps
+// are dealt round-robin to the waves; every wave streams its steps through
+// registers, keeping the next step's K and V in flight while the current one
 // is consumed, and carries its own online-softmax state per row.  The waves
 // are merged at the end through LDS with the log-sum-exp algebra, in a fixed
-// order (no atomics: runs are bit-reproducible).
+// order (no atomics: runs are bit-reproducible).  In split mode over many
+// partitions (kWavePart) each wave owns a whole partition instead and writes
+// its partial itself.
 //
-// Per 16-token block, everything is two small matrix products whose operands
-// come straight from the loads (lane l: r = l % 16, q = l / 16):
+// A step is 16 tokens: one 16-token block, or two 8-token blocks (kBS = 8;
+// lanes r < 8 then read the first block's tile, r >= 8 the second's, see load).
+// Per step, everything is two small matrix products whose operands come
+// straight from the loads (lane l: r = l % 16, q = l / 16):
 //
-//   logits  S^T[token][head] = K[token][:] . Q[head][:]        (16 x 16 x d)
+//   logits  S^T[token][row] = K[token][:] . Q[row][:]          (16 x 16 x d)
 //           A = K tile: the pool stores K chunk-major ([d/x][16][x], x elements
 //               per 16 bytes), so load j of a tile is the contiguous 1 KiB
 //               tile[64 j + lane] = chunk 4j + q of token r: exactly lane l's
@@ -29,19 +33,22 @@
 //           B = Q: lane l holds chunk 4j + q of query row r of the chunk (zero
 //               rows pad the chunk to 16).
 //           out: lane l holds the logits of tokens 4q .. 4q+3 for row r.
-//   P.V     O^T[col][head] += V^T[col][token] . P^T[token][head]   (16 x 16 x 16 per 16 columns)
+//   P.V     O^T[col][row] += V^T[col][token] . P^T[token][row]   (16 x 16 x 16 per 16 columns)
 //           A = V tile: the pool stores V head-dim-major ([d][16]), so lane l's
 //               operand (tokens 4q .. 4q+3 of column 16 cb + r) is one
 //               contiguous 4-element load, and the 64 lanes read 64 * 4
 //               contiguous elements.
 //           B = P: lane l already holds the weights of tokens 4q .. 4q+3 for
-//               head r -- the logits' own output layout -- so P never moves.
+//               row r -- the logits' own output layout -- so P never moves.
 //           out: lane l holds O[row r][16 cb + 4q .. 16 cb + 4q + 3].
+//
+// Int8 keys (MmaK8) feed the same logits product with f16 operands: the codes
+// convert exactly and the per-channel scales ride on the query (see MmaK8).
 //
 // Online softmax (§4.2 of the ialgorithm.me page: the normaliser is updated
 // while streaming, exactly): the running maximum m of each row is shared by
-// the four lanes holding that row (two lane-swap max steps per block).  m is
-// only raised when a block's maximum exceeds it by more than kSlack (log2
+// the four lanes holding that row (two lane-swap max steps per step).  m is
+// only raised when a step's maximum exceeds it by more than kSlack (log2
 // units); until then weights up to 2^kSlack are accumulated as they are.  The
 // result is the same algebra (every partial sum uses one common reference), and
 // the rescale of the accumulators becomes rare.  Weights are rounded to the KV
@@ -73,7 +80,7 @@ constexpr float kSlack = 8.0f;  // log2 headroom before the running maximum is r
 // Load-ring depth and cache policy (compile-time; the defaults are the
 // measured best on MI355X).  Waves per workgroup are chosen per call.
 #ifndef PA_DECODE_DEPTH
-#define PA_DECODE_DEPTH 2  // 16-token blocks per wave in the load ring
+#define PA_DECODE_DEPTH 2  // 16-token steps per wave in the load ring
 #endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1  // streaming (non-temporal) hint on 1: K and V, 2: K, 3: V loads
