@@ -7,7 +7,6 @@
 
 namespace {
 
-constexpr int kMaxReduceParts = 8192;  // partition weights staged in 32 KiB of LDS
 constexpr int kMaxQueryTokens = 256;   // draft tokens per sequence in one verify call
 
 bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -264,12 +263,13 @@ pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t 
   if (partition_size <= 0 || partition_size % pa::kStep != 0) return PA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (elem_bytes(out_dtype) == 0 || is_k8(out_dtype)) return PA_ERR_UNSUPPORTED;
-  if (num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   if (!aligned(workspace, 16) || !aligned(out, 16) || !aligned(context_lens, 4))
     return PA_ERR_MISALIGNED;
+  // one 64-lane wavefront per 32 output columns of a row: the threads must fit a 1-D grid
+  if (static_cast<int64_t>(num_seqs) * num_q_heads * (head_dim / 32) * 64 > INT32_MAX)
+    return PA_ERR_UNSUPPORTED;
   pa::ReduceArgs a{};
   a.num_parts = num_parts_for(max_context_len, partition_size);
-  if (a.num_parts > kMaxReduceParts) return PA_ERR_UNSUPPORTED;
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * a.num_parts;
   a.o_part = static_cast<const float*>(workspace);
   a.lse_part = a.o_part + rows * head_dim;

@@ -8,120 +8,119 @@ namespace pa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// pa_reduce: one workgroup of 256 threads per (sequence, query head).  The
+// pa_reduce: one wavefront per (row, 32-column slice), four per workgroup.  The
 // partition results are re-weighted by their share of the softmax mass: with
 // M = max lse_p, weight_p = exp(lse_p - M) / sum_q exp(lse_q - M).  This is the
 // same streaming-normaliser identity that makes the online softmax exact (§4.2
 // of the ialgorithm.me page).
-//   1. weights: thread p < live partitions computes exp(lse_p - M) into LDS
-//      (M and the sum by a fixed-order block reduction);
-//   2. thread t owns 4 columns (t % (D/4)) and every G-th partition starting
-//      at t / (D/4), with G = 256 / (D/4) partition groups, float4 loads (the
-//      first eight of them issued before step 1, since they need no weight);
-//   3. the G group sums are added in group order through LDS.
-// Every sum has a fixed order, so the result is bit-reproducible.
+//   lane l = 8 g + c: float4 column c of the slice, partitions g, g + 8, ...;
+//   1. the first kPre partials of the lane and their lse are loaded before
+//      anything else (they need no weight), the maximum M is a lane-strided
+//      scan of the live lse values and a butterfly over the wavefront;
+//   2. each lane weights and sums its partitions and their weights;
+//   3. a butterfly over the eight partition groups (lane bits 3..5) adds the
+//      group sums; lanes 0..7 normalise and store.
+// No LDS and no barrier.  Every sum has a fixed order and the butterfly gives
+// every lane the same bits, so the result is reproducible run to run.
 // ---------------------------------------------------------------------------
-constexpr int kReduceThreads = 256;
-
-__device__ __forceinline__ float block_max_256(float v, float* sm) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
-  __syncthreads();
-  v = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
-  __syncthreads();
-  return v;
-}
+constexpr int kReduceWaves = 4;    // wavefronts per workgroup
+constexpr int kSliceCols = 32;     // output columns per wavefront
+constexpr int kPartGroups = 8;     // partition groups per wavefront (x 8 float4 columns = 64 lanes)
 
 template <class Tr, int D>
-__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
-  constexpr int kCols4 = D / 4;                       // float4 column groups
-  constexpr int kGroups = kReduceThreads / kCols4;    // partition groups
-  constexpr int kPre = 8;                             // partials loaded before the weights
-  extern __shared__ float sm_w[];                     // [num_parts] weights
-  __shared__ float sm_red[4];
-  __shared__ float4 sm_acc[kGroups][kCols4];
+__global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a) {
+  constexpr int kSlices = D / kSliceCols;
+  constexpr int kPre = 8;  // partials per lane loaded up front
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kReduceWaves + (threadIdx.x >> 6);
+  if (unit >= static_cast<int64_t>(a.num_seqs) * a.num_q_heads * kSlices) return;
+  const int64_t row = unit / kSlices;
+  const int slice = static_cast<int>(unit % kSlices);
+  const int s = static_cast<int>(row / a.num_q_heads);
+  const int c4 = lane % (kSliceCols / 4);
+  const int grp = lane / (kSliceCols / 4);
+  const int col = slice * kSliceCols + 4 * c4;
+  const float* lse = a.lse_part + row * a.num_parts;
+  const float* op = a.o_part + row * a.num_parts * D + col;
 
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int t = threadIdx.x;
-  const size_t row = static_cast<size_t>(s) * a.num_q_heads + h;
-  const int c4 = t % kCols4;
-  const int grp = t / kCols4;
-  const float4* op = reinterpret_cast<const float4*>(a.o_part + row * a.num_parts * D) + c4;
-  // The first kPre partials of this thread do not depend on the weights (every
-  // partition of the workspace was written, empty ones as zeros): issue their
-  // loads first so they overlap the lse loads and the max reduction.
   float4 pre[kPre];
+  float lpre[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) {
-    const int p = grp + i * kGroups;
-    pre[i] = p < a.num_parts ? op[static_cast<size_t>(p) * kCols4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int p = grp + i * kPartGroups;
+    if (p < a.num_parts) {
+      pre[i] = *reinterpret_cast<const float4*>(op + static_cast<size_t>(p) * D);
+      lpre[i] = lse[p];
+    } else {
+      pre[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      lpre[i] = -INFINITY;
+    }
   }
   const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
   const int nv = (L + a.partition_tokens - 1) / a.partition_tokens;  // live partitions
-  const float* lse = a.lse_part + row * a.num_parts;
 
-  float mx = -INFINITY;
-  for (int p = t; p < nv; p += kReduceThreads) mx = fmaxf(mx, lse[p]);
-  const float M = block_max_256(mx, sm_red);
-  if (M == -INFINITY) {  // empty context: zero row (block-uniform branch)
-    for (int c = t; c < D; c += kReduceThreads) Tr::store(a.out, row * D + c, 0.f);
-    return;
-  }
-  for (int p = t; p < nv; p += kReduceThreads) sm_w[p] = __expf(lse[p] - M);
-  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll 4
+  for (int p = lane; p < nv; p += 64) M = fmaxf(M, lse[p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float wsum = 0.f;
+  if (M != -INFINITY) {  // wavefront-uniform: an empty context stores a zero row
 #pragma unroll
-  for (int i = 0; i < kPre; ++i) {
-    const int p = grp + i * kGroups;
-    if (p < nv) {
-      const float w = sm_w[p];
-      acc.x = fmaf(w, pre[i].x, acc.x);
-      acc.y = fmaf(w, pre[i].y, acc.y);
-      acc.z = fmaf(w, pre[i].z, acc.z);
-      acc.w = fmaf(w, pre[i].w, acc.w);
+    for (int i = 0; i < kPre; ++i) {
+      if (grp + i * kPartGroups < nv) {
+        const float w = __expf(lpre[i] - M);
+        acc.x = fmaf(w, pre[i].x, acc.x);
+        acc.y = fmaf(w, pre[i].y, acc.y);
+        acc.z = fmaf(w, pre[i].z, acc.z);
+        acc.w = fmaf(w, pre[i].w, acc.w);
+        wsum += w;
+      }
     }
-  }
-  for (int p = grp + kPre * kGroups; p < nv; p += kGroups) {
-    const float w = sm_w[p];
-    const float4 v = op[static_cast<size_t>(p) * kCols4];
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
-  }
-  sm_acc[grp][c4] = acc;
-  __syncthreads();
-  if (t < kCols4) {
-    float wsum = 0.f;
-    for (int p = 0; p < nv; ++p) wsum += sm_w[p];
+#pragma unroll 4
+    for (int p = grp + kPre * kPartGroups; p < nv; p += kPartGroups) {
+      const float w = __expf(lse[p] - M);
+      const float4 v = *reinterpret_cast<const float4*>(op + static_cast<size_t>(p) * D);
+      acc.x = fmaf(w, v.x, acc.x);
+      acc.y = fmaf(w, v.y, acc.y);
+      acc.z = fmaf(w, v.z, acc.z);
+      acc.w = fmaf(w, v.w, acc.w);
+      wsum += w;
+    }
+#pragma unroll
+    for (int off = kSliceCols / 4; off < 64; off <<= 1) {
+      acc.x += __shfl_xor(acc.x, off);
+      acc.y += __shfl_xor(acc.y, off);
+      acc.z += __shfl_xor(acc.z, off);
+      acc.w += __shfl_xor(acc.w, off);
+      wsum += __shfl_xor(wsum, off);
+    }
     const float inv = 1.f / wsum;
-    float4 o = sm_acc[0][t];
-#pragma unroll
-    for (int g = 1; g < kGroups; ++g) {
-      o.x += sm_acc[g][t].x;
-      o.y += sm_acc[g][t].y;
-      o.z += sm_acc[g][t].z;
-      o.w += sm_acc[g][t].w;
-    }
-    const size_t base = row * D + 4 * t;
-    Tr::store(a.out, base + 0, o.x * inv);
-    Tr::store(a.out, base + 1, o.y * inv);
-    Tr::store(a.out, base + 2, o.z * inv);
-    Tr::store(a.out, base + 3, o.w * inv);
+    acc.x *= inv;
+    acc.y *= inv;
+    acc.z *= inv;
+    acc.w *= inv;
+  }
+  if (grp == 0) {
+    const size_t base = static_cast<size_t>(row) * D + col;
+    Tr::store(a.out, base + 0, acc.x);
+    Tr::store(a.out, base + 1, acc.y);
+    Tr::store(a.out, base + 2, acc.z);
+    Tr::store(a.out, base + 3, acc.w);
   }
 }
 
 template <class Tr>
 hipError_t launch_reduce_t(const ReduceArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_q_heads, a.num_seqs);
-  const size_t lds = static_cast<size_t>(a.num_parts) * sizeof(float);
+  const int slices = a.head_dim / kSliceCols;
+  const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_q_heads * slices;
+  const dim3 grid(static_cast<uint32_t>((units + kReduceWaves - 1) / kReduceWaves));
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((reduce_kernel<Tr, 64>), grid, dim3(kReduceThreads), lds, stream, a);
+    hipLaunchKernelGGL((reduce_kernel<Tr, 64>), grid, dim3(64 * kReduceWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((reduce_kernel<Tr, 128>), grid, dim3(kReduceThreads), lds, stream, a);
+    hipLaunchKernelGGL((reduce_kernel<Tr, 128>), grid, dim3(64 * kReduceWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -181,6 +181,33 @@ def test_decode_random_cases(case):
         assert not o_p[~live].any()
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("f16", 128)])
+def test_reduce_many_partitions(dtype, d):
+    """16-token partitions over up to 3000 tokens: 188 partials per row, more
+    than the merge kernel loads up front (64 per 32-column slice), with an
+    empty and a one-partition context in the same batch.  End to end against
+    the oracle, and pa_reduce alone against the oracle's merge of the GPU's own
+    partials."""
+    lens = [3000, 0, 1500, 16, 2047]
+    P = 16
+    w = wl.make_random_case(530 + d, num_seqs=len(lens), num_q_heads=8, num_kv_heads=2,
+                            head_dim=d, dtype=dtype, lens=lens, partition_size=P)
+    dw = upload(w, DEV)
+    out, ws = run_decode(dw, P)
+    got = widen_f32(out)
+    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                               w.scale, dtype)
+    assert_close(got, want, TOL[dtype], f"{dtype} d{d} P{P}")
+    n_parts = oracle.num_partitions(w.max_context_len, P)
+    o_p, lse_p = split_workspace(ws, w.num_seqs, 8, d, n_parts)
+    merged = oracle.merge_partials(o_p, lse_p)
+    # out rounds once to its dtype; the merge itself is float32 with exp2-based weights
+    ulp = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[dtype]
+    bound = np.abs(merged) * ulp + 1e-5
+    assert (np.abs(got - merged) <= bound).all(), np.abs(got - merged).max()
+    assert not got[1].any()
+
+
 # ---------------------------------------------------------------------------
 # decode parity on the five workloads at full size
 # ---------------------------------------------------------------------------
