@@ -96,7 +96,8 @@ def test_reduce_and_other_calls_reject_bad_arguments(lib):
     assert r(FAKE, FAKE, 2, 4, 96, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
     assert r(FAKE, FAKE, 2, 4, 64, 40, 16, 9, FAKE, None) == pa.PA_ERR_UNSUPPORTED
     assert r(FAKE + 4, FAKE, 2, 4, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_MISALIGNED
-    assert r(FAKE, FAKE, 2, 4, 64, 16 * 9000, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    # one wavefront per 32 columns of a row: more than a 1-D grid holds is refused
+    assert r(FAKE, FAKE, 1 << 20, 64, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
     d = _desc()
     assert lib.pa_init_pool(ctypes.byref(d), None, FAKE, 0, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_init_pool(ctypes.byref(d), FAKE, FAKE, 2, None) == pa.PA_ERR_INVALID_ARG
