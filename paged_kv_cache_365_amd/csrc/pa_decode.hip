@@ -309,9 +309,20 @@ __device__ __forceinline__ Unit unit_of(int id, int total, int wgs, int parts, i
   return u;
 }
 
+// Wavefronts per SIMD the register allocation must leave room for (512
+// registers per lane and SIMD): the ring of kDepth steps, the accumulators and
+// the query operands of a lane fit 168 registers at d 128 with one chunk (three
+// waves), 256 with two; float32 tiles are twice as large.
+template <class M, int D, int kChunks>
+constexpr int min_waves_per_simd() {
+  if constexpr (M::kKBytes == 4) return D == 128 ? 2 : (kChunks == 1 ? 3 : 2);
+  return D == 128 ? (kChunks == 1 ? 3 : 2) : (kChunks == 1 ? 5 : 3);
+}
+
 template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared, int kBS,
           bool kWavePart>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>())) void decode_kernel(
+    DecodeArgs a) {
   // Sibling workgroups (kShared) read each tile through the XCD's L2 one after
   // another, so their loads must not carry the streaming hint.
   constexpr bool kStreamK = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 2);
@@ -521,41 +532,54 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  // A ring of kDepth register sets: the wave's i-th step (blk_lo + wave + i *
-  // kWaves when the waves share a partition, blk_lo + i when the wave owns it)
-  // is consumed while steps i+1 .. i+kDepth-1 are in flight.  The physical id
-  // of the step to load next is read one iteration before its tile loads are
-  // issued.
+  // The wave's steps are jb(i) = first + i * kStride, i in [0, n) (kStride =
+  // kWaves when the waves share a partition, 1 when the wave owns it).  A ring
+  // of kDepth register sets: step i is consumed while steps i+1 .. i+kDepth-1
+  // are in flight; the physical id of the step to load next is read one step
+  // before its tile loads are issued.  Every load below is issued
+  // unconditionally on its path (the last steps get one branch per count), so
+  // the wait before each consume covers exactly the step consumed: a load that
+  // may or may not have been issued would make the compiler wait for every
+  // load in flight, the next steps' included.
   uint4 kr[kDepth][kKLoads];
   VLoad vr[kDepth][kColBlocks];
   const int first = blk_lo + (kWavePart ? 0 : wave);
-  Phys next_phys{0, 0};
+  const int n = first < blk_hi ? (blk_hi - first + kStride - 1) / kStride : 0;
+  auto step_of = [&](int i) { return first + i * kStride; };
+  if (n > 0) {  // wave-uniform
+    // prologue: steps 0 .. kDepth-2 (an index past the last step reloads it)
 #pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d) {
-    const int jb = first + d * kStride;
-    if (jb < blk_hi) load(physical(jb), kr[d], vr[d]);
-  }
-  {
-    const int jb = first + (kDepth - 1) * kStride;
-    if (jb < blk_hi) next_phys = physical(jb);
-  }
-  for (int base = 0;; base += kDepth) {
-    bool done = false;
+    for (int d = 0; d < kDepth - 1; ++d) load(physical(step_of(min(d, n - 1))), kr[d], vr[d]);
+    Phys next_phys = physical(step_of(min(kDepth - 1, n - 1)));
+    int base = 0;
+    // steady state: every step entering the ring exists
+    for (; base + 2 * kDepth - 1 <= n; base += kDepth) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int jb = first + (base + u) * kStride;
-      if (jb >= blk_hi) {
-        done = true;
-        break;
-      }
-      const int jn = jb + (kDepth - 1) * kStride;  // the step entering the ring
-      if (jn < blk_hi) {
+      for (int u = 0; u < kDepth; ++u) {
+        const int in = base + u + kDepth - 1;  // the step entering the ring
         load(next_phys, kr[(u + kDepth - 1) % kDepth], vr[(u + kDepth - 1) % kDepth]);
-        if (jn + kStride < blk_hi) next_phys = physical(jn + kStride);
+        next_phys = physical(step_of(min(in + 1, n - 1)));
+        consume(step_of(base + u), kr[u], vr[u]);
       }
-      consume(jb, kr[u], vr[u]);
     }
-    if (done) break;
+    // the last r = n - base <= 2 kDepth - 2 steps (base is a multiple of
+    // kDepth, so step base + u sits in ring slot u % kDepth), one branch per r
+    // so that every load inside it is unconditional as well
+    const int r = n - base;
+#pragma unroll
+    for (int R = 1; R <= 2 * kDepth - 2; ++R) {
+      if (r == R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+          const int in = u + kDepth - 1;
+          if (in < R) {
+            load(next_phys, kr[in % kDepth], vr[in % kDepth]);
+            if (in + 1 < R) next_phys = physical(step_of(base + in + 1));
+          }
+          consume(step_of(base + u), kr[u % kDepth], vr[u % kDepth]);
+        }
+      }
+    }
   }
 
   if constexpr (kWavePart) {
