@@ -208,6 +208,22 @@ def test_reduce_many_partitions(dtype, d):
     assert not got[1].any()
 
 
+@pytest.mark.parametrize("P", [0, 256, 2048])
+def test_long_context_full_oracle(P):
+    """A 131072-token context (four times the long-context workload) next to a
+    70001-token one, against the full oracle: 8192 steps for one (sequence, KV
+    head) unsplit, 512 one-wave partitions at P = 256, 64 shared partitions at
+    P = 2048."""
+    w = wl.make_random_case(1201, num_seqs=2, num_q_heads=8, num_kv_heads=1, head_dim=128,
+                            dtype="bf16", lens=[131072, 70001], free_fraction=0.02,
+                            partition_size=P)
+    dw = upload(w, DEV)
+    out, _ = run_decode(dw, P)
+    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                               w.scale, "bf16")
+    assert_close(widen_f32(out), want, TOL["bf16"], f"131072 tokens P{P}")
+
+
 # ---------------------------------------------------------------------------
 # decode parity on the five workloads at full size
 # ---------------------------------------------------------------------------

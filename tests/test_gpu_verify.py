@@ -81,6 +81,25 @@ def test_verify_random_cases(case):
         assert_close(o_p[live], wo[live], TOL[dtype], "partials")
 
 
+@pytest.mark.parametrize("P", [0, 64])
+def test_verify_longest_draft(P):
+    """The longest draft the call takes (256 tokens): 512 rows per KV head, 16
+    sibling workgroups of two chunks, contexts shorter than, equal to and
+    longer than the draft."""
+    T, hq, hkv, d = 256, 4, 2, 64
+    lens = [1, 255, 256, 257, 400]
+    w = wl.make_random_case(1202, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=d, dtype="bf16", lens=lens)
+    dw = upload(w, DEV)
+    q = queries(1203, len(lens), T, hq, d, "bf16")
+    out = pa.verify_attention(to_torch(q, "bf16", DEV), dw.k_pool, dw.v_pool, dw.block_tables,
+                              dw.context_lens, w.max_context_len, w.scale, partition_size=P)
+    torch.cuda.synchronize()
+    want = oracle.paged_verify(q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                               "bf16")
+    assert_close(widen_f32(out), want, TOL["bf16"], f"T{T} P{P}")
+
+
 @pytest.mark.parametrize("dtype,hq,hkv,T,P", [("bf16", 64, 8, 4, 0), ("f16", 16, 2, 3, 32),
                                               ("f32", 8, 2, 2, 0)])
 def test_verify_row_equals_sequential_decode(dtype, hq, hkv, T, P):
