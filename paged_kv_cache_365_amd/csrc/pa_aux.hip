@@ -62,8 +62,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a)
   float M = -INFINITY;
 #pragma unroll 4
   for (int p = lane; p < nv; p += 64) M = fmaxf(M, lse[p]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  M = across_groups_max<1>(M);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.f;
@@ -89,14 +88,12 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a)
       acc.w = fmaf(w, v.w, acc.w);
       wsum += w;
     }
-#pragma unroll
-    for (int off = kSliceCols / 4; off < 64; off <<= 1) {
-      acc.x += __shfl_xor(acc.x, off);
-      acc.y += __shfl_xor(acc.y, off);
-      acc.z += __shfl_xor(acc.z, off);
-      acc.w += __shfl_xor(acc.w, off);
-      wsum += __shfl_xor(wsum, off);
-    }
+    constexpr int kGroupLanes = kSliceCols / 4;  // lanes of one partition group
+    acc.x = across_groups_sum<kGroupLanes>(acc.x);
+    acc.y = across_groups_sum<kGroupLanes>(acc.y);
+    acc.z = across_groups_sum<kGroupLanes>(acc.z);
+    acc.w = across_groups_sum<kGroupLanes>(acc.w);
+    wsum = across_groups_sum<kGroupLanes>(wsum);
     const float inv = 1.f / wsum;
     acc.x *= inv;
     acc.y *= inv;

@@ -97,31 +97,6 @@ __device__ __forceinline__ int pa_clamp_len(int len, int max_len) {
 // ---------------------------------------------------------------------------
 // cross-lane reductions
 // ---------------------------------------------------------------------------
-// DPP control words (GFX9 encoding)
-constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
-constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16-lane row
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-
-// Sum over groups of kWidth consecutive lanes (kWidth in 1..64, a power of
-// two); every lane of a group receives the group's sum.  Steps inside a 16-lane
-// row use DPP; wider groups use cross-row shuffles.
-template <int kWidth>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (kWidth >= 2) v += dpp<kDppQuadXor1>(v);
-  if constexpr (kWidth >= 4) v += dpp<kDppQuadXor2>(v);
-  if constexpr (kWidth >= 8) v += dpp<kDppRowHalfMirror>(v);
-  if constexpr (kWidth >= 16) v += dpp<kDppRowMirror>(v);
-  if constexpr (kWidth >= 32) v += __shfl_xor(v, 16);
-  if constexpr (kWidth >= 64) v += __shfl_xor(v, 32);
-  return v;
-}
-
 // Reduction across the groups of kWidth lanes (lanes with equal lane % kWidth).
 template <int kWidth>
 __device__ __forceinline__ float across_groups_max(float v) {
