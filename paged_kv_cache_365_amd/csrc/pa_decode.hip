@@ -7,8 +7,10 @@
 // sequence that share KV head g (G = query heads per KV head) read the same K/V
 // tiles, so they are computed together: 16 rows per matrix-core chunk, kChunks
 // chunks per workgroup (two at most), and each tile is loaded once for all of
-// them.  More rows than that go to sibling workgroups placed on one XCD, which
-// read the tiles through that XCD's L2 (see unit_of).
+// them.  With 16-bit keys, more than 32 rows go to workgroups of 64 whose four
+// waves hold one chunk each and share every tile through LDS (kLds).  Rows
+// beyond one workgroup go to sibling workgroups placed on one XCD, which read
+// the tiles through that XCD's L2 (see unit_of).
 //
 // Work unit.  A workgroup of kWaves wavefronts owns (sequence s, KV head g, up
 // to 16 * kChunks of g's rows, partition p).  The partition's 16-token steps
@@ -320,9 +322,16 @@ constexpr int min_waves_per_simd() {
 }
 
 template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared, int kBS,
-          bool kWavePart>
+          bool kWavePart, bool kLds = false>
 __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>())) void decode_kernel(
     DecodeArgs a) {
+  // kLds: four waves hold the four 16-row chunks of 64 rows and share each
+  // step's tile through an LDS ring (see below); otherwise every wave holds all
+  // kChunks chunks of the workgroup's rows and the waves split the steps.
+  static_assert(!kLds || (kWaves == 4 && kChunks == 1 && !kWavePart), "LDS ring: 4 x 16 rows");
+  constexpr int kRowWaves = kLds ? 4 : 1;            // waves that split the rows
+  constexpr int kStepWaves = kWaves / kRowWaves;     // waves that split the steps
+  constexpr int kWgRows = 16 * kChunks * kRowWaves;  // rows of one workgroup
   // Sibling workgroups (kShared) read each tile through the XCD's L2 one after
   // another, so their loads must not carry the streaming hint.
   constexpr bool kStreamK = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 2);
@@ -334,22 +343,24 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // kWavePart (split mode): each wave owns one whole partition and writes its
   // partial itself, so a workgroup covers kWaves consecutive partitions with
   // no merge through LDS; otherwise the waves share one partition's blocks.
-  constexpr int kStride = kWavePart ? 1 : kWaves;  // logical-step stride of a wave
+  constexpr int kStride = kWavePart ? 1 : kStepWaves;  // logical-step stride of a wave
   using VLoad = typename M::VLoad;
 
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int qg = lane >> 4;
   const int wave = wave_id();
+  const int rw = wave % kRowWaves;  // this wave's chunk of the workgroup's rows
+  const int sw = wave / kRowWaves;  // this wave's share of the steps
   const int T = a.num_query_tokens;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int rows = T * group;  // (query token, query head) rows that read KV head g
-  const int wgs = (rows + 16 * kChunks - 1) / (16 * kChunks);
+  const int wgs = (rows + kWgRows - 1) / kWgRows;
   const int part_units = kWavePart ? (a.num_parts + kWaves - 1) / kWaves : a.num_parts;
   const Unit u = unit_of(blockIdx.x, gridDim.x, wgs, part_units, a.num_kv_heads);
   const int part = kWavePart ? u.part * kWaves + wave : u.part;
   const int g = u.kv_head;
-  const int row0 = u.sibling * (16 * kChunks);
+  const int row0 = u.sibling * kWgRows + rw * (16 * kChunks);
   const int s = u.seq;
   if (kWavePart && part >= a.num_parts) return;  // a wave past the last partition (no barriers)
 
@@ -464,31 +475,41 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
     return p;
   };
 
-  auto load = [&](Phys ph, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
+  // Per-lane tile pointers of a step and the addresses of its K operand j and
+  // V operand cb.  8-token tiles: K token r of the step is token r % 8 of
+  // block r / 8 (the lane's chunk 4j + qg at [chunk][r % 8]: 512 contiguous
+  // bytes per half wave); V tokens 4qg .. 4qg+3 are tokens 4 (qg % 2) .. of
+  // block qg / 2.
+  struct TilePtrs {
+    const uint4* kt;
+    const VLoad* vt;
+  };
+  auto tile_ptrs = [&](Phys ph) {
+    TilePtrs p;
     if constexpr (kBS == 16) {
       const size_t tile = pa_tile_offset(ph.a, g, a.num_kv_heads, D, 16);  // elements
-      const uint4* kt = reinterpret_cast<const uint4*>(kbase + tile * M::kKBytes);
-      const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + tile * M::kVBytes);
-#pragma unroll
-      for (int j = 0; j < kKLoads; ++j) kr[j] = load16<kStreamK>(kt + 64 * j + lane);
-#pragma unroll
-      for (int cb = 0; cb < kColBlocks; ++cb)
-        vr[cb] = load16<kStreamV>(vt + (16 * cb + r) * 4 + qg);
+      p.kt = reinterpret_cast<const uint4*>(kbase + tile * M::kKBytes);
+      p.vt = reinterpret_cast<const VLoad*>(vbase + tile * M::kVBytes);
     } else {
-      // 8-token tiles: K token r of the step is token r % 8 of block r / 8 (the
-      // lane's chunk 4j + qg at [chunk][r % 8]: 512 contiguous bytes per half
-      // wave); V tokens 4qg .. 4qg+3 are tokens 4 (qg % 2) .. of block qg / 2.
       const size_t ta = pa_tile_offset(ph.a, g, a.num_kv_heads, D, 8);
       const size_t tb = pa_tile_offset(ph.b, g, a.num_kv_heads, D, 8);
-      const uint4* kt = reinterpret_cast<const uint4*>(kbase + (r < 8 ? ta : tb) * M::kKBytes);
-      const VLoad* vt = reinterpret_cast<const VLoad*>(vbase + (qg < 2 ? ta : tb) * M::kVBytes);
-#pragma unroll
-      for (int j = 0; j < kKLoads; ++j)
-        kr[j] = load16<kStreamK>(kt + (4 * j + qg) * 8 + (r & 7));
-#pragma unroll
-      for (int cb = 0; cb < kColBlocks; ++cb)
-        vr[cb] = load16<kStreamV>(vt + (16 * cb + r) * 2 + (qg & 1));
+      p.kt = reinterpret_cast<const uint4*>(kbase + (r < 8 ? ta : tb) * M::kKBytes);
+      p.vt = reinterpret_cast<const VLoad*>(vbase + (qg < 2 ? ta : tb) * M::kVBytes);
     }
+    return p;
+  };
+  auto k_at = [&](const TilePtrs& p, int j) {
+    return kBS == 16 ? p.kt + 64 * j + lane : p.kt + (4 * j + qg) * 8 + (r & 7);
+  };
+  auto v_at = [&](const TilePtrs& p, int cb) {
+    return kBS == 16 ? p.vt + (16 * cb + r) * 4 + qg : p.vt + (16 * cb + r) * 2 + (qg & 1);
+  };
+  auto load = [&](Phys ph, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
+    const TilePtrs p = tile_ptrs(ph);
+#pragma unroll
+    for (int j = 0; j < kKLoads; ++j) kr[j] = load16<kStreamK>(k_at(p, j));
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = load16<kStreamV>(v_at(p, cb));
   };
 
   auto consume = [&](int jb, const uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
@@ -543,10 +564,77 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // load in flight, the next steps' included.
   uint4 kr[kDepth][kKLoads];
   VLoad vr[kDepth][kColBlocks];
-  const int first = blk_lo + (kWavePart ? 0 : wave);
+  const int first = blk_lo + (kWavePart ? 0 : sw);
   const int n = first < blk_hi ? (blk_hi - first + kStride - 1) / kStride : 0;
   auto step_of = [&](int i) { return first + i * kStride; };
-  if (n > 0) {  // wave-uniform
+  if constexpr (kLds) {
+    // The four waves hold the four 16-row chunks of the workgroup's 64 rows
+    // and walk the same steps.  Each step's tile is read from memory once:
+    // wave w loads K operands w, w + 4, ... and V operands w, w + 4, ... (for
+    // every lane), writes them to a two-slot LDS ring, and after one barrier
+    // every wave reads the whole tile back as its own operands.
+    constexpr int kKS = (kKLoads + 3) / 4;
+    constexpr int kVS = (kColBlocks + 3) / 4;
+    constexpr int kAhead = 2;  // steps staged in registers ahead of the LDS ring
+    __shared__ uint4 lds_k[2][kKLoads][64];
+    __shared__ VLoad lds_v[2][kColBlocks][64];
+    uint4 sk[kAhead][kKS];
+    VLoad sv[kAhead][kVS];
+    auto stage = [&](Phys ph, uint4 (&k)[kKS], VLoad (&v)[kVS]) {
+      const TilePtrs p = tile_ptrs(ph);
+#pragma unroll
+      for (int i = 0; i < kKS; ++i) k[i] = load16<kStreamK>(k_at(p, min(wave + 4 * i, kKLoads - 1)));
+#pragma unroll
+      for (int i = 0; i < kVS; ++i)
+        v[i] = load16<kStreamV>(v_at(p, min(wave + 4 * i, kColBlocks - 1)));
+    };
+    const int nl = blk_hi - blk_lo;  // workgroup-uniform: every wave walks every step
+    if (nl > 0) {
+      // in step order (the waits below count on step d's loads being older
+      // than step d + 1's)
+#pragma unroll
+      for (int d = 0; d < kAhead; ++d) {
+        stage(physical(blk_lo + min(d, nl - 1)), sk[d], sv[d]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      Phys next = physical(blk_lo + min(kAhead, nl - 1));
+      // one step: publish its staged tile share, stage the step kAhead ahead
+      // (the last one again past the end: no branch, so the waits before the
+      // ring writes stay exact), barrier, read the whole tile back, compute
+      auto lds_step = [&](int i, uint4 (&k)[kKS], VLoad (&v)[kVS], int slot) {
+        // (with fewer than four operands of a kind, two waves load and write
+        // the same one: equal values, so the duplicate write is harmless)
+#pragma unroll
+        for (int t = 0; t < kKS; ++t) lds_k[slot][min(wave + 4 * t, kKLoads - 1)][lane] = k[t];
+#pragma unroll
+        for (int t = 0; t < kVS; ++t) lds_v[slot][min(wave + 4 * t, kColBlocks - 1)][lane] = v[t];
+        stage(next, k, v);
+        next = physical(blk_lo + min(i + kAhead + 1, nl - 1));
+        __syncthreads();
+        uint4 kr[kKLoads];
+        VLoad vr[kColBlocks];
+#pragma unroll
+        for (int j = 0; j < kKLoads; ++j) kr[j] = lds_k[slot][j][lane];
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = lds_v[slot][cb][lane];
+        if (row0 < rows) consume(blk_lo + i, kr, vr);
+      };
+      int base = 0;
+      for (; base + kAhead <= nl; base += kAhead) {
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) lds_step(base + u, sk[u], sv[u], u & 1);
+      }
+      const int rem = nl - base;  // workgroup-uniform, < kAhead; one branch per count
+#pragma unroll
+      for (int R = 1; R < kAhead; ++R) {
+        if (rem == R) {
+#pragma unroll
+          for (int u = 0; u < R; ++u) lds_step(base + u, sk[u], sv[u], u & 1);
+        }
+      }
+    }
+  }
+  if (!kLds && n > 0) {  // wave-uniform
     // prologue: steps 0 .. kDepth-2 (an index past the last step reloads it)
 #pragma unroll
     for (int d = 0; d < kDepth - 1; ++d) load(physical(step_of(min(d, n - 1))), kr[d], vr[d]);
@@ -582,8 +670,9 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
     }
   }
 
-  if constexpr (kWavePart) {
-    // this wave's partition: normalise in registers and write the partial
+  if constexpr (kWavePart || kLds) {
+    // every row of this wave lives in this wave alone (its own partition, or
+    // its own chunk of the workgroup's rows): normalise in registers and write
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int rho = row0 + 16 * c + r;
@@ -593,12 +682,19 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
       const float inv = seen ? 1.f / ls : 0.f;
       const size_t row = (static_cast<size_t>(s) * T + rho / group) * a.num_q_heads +
                          g * group + rho % group;
-      float* op = a.o_part + (row * a.num_parts + part) * D + 4 * qg;
+      if (a.write_partials) {
+        float* op = a.o_part + (row * a.num_parts + part) * D + 4 * qg;
 #pragma unroll
-      for (int cb = 0; cb < kColBlocks; ++cb)
-        *reinterpret_cast<f32x4*>(op + 16 * cb) = acc[c][cb] * inv;
-      if (qg == 0)
-        a.lse_part[row * a.num_parts + part] = seen ? (m[c] + __log2f(ls)) * kLn2 : -INFINITY;
+        for (int cb = 0; cb < kColBlocks; ++cb)
+          *reinterpret_cast<f32x4*>(op + 16 * cb) = acc[c][cb] * inv;
+        if (qg == 0)
+          a.lse_part[row * a.num_parts + part] = seen ? (m[c] + __log2f(ls)) * kLn2 : -INFINITY;
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Tr::store(a.out, row * D + 16 * cb + 4 * qg + i, acc[c][cb][i] * inv);
+      }
     }
     return;
   }
@@ -714,8 +810,35 @@ hipError_t launch_c(const DecodeArgs& a, hipStream_t stream) {
   return launch_cs<M, Tr, D, kChunks, false, 16>(a, wgs, stream);
 }
 
+// More than 32 rows per KV head with 16-bit keys: workgroups of 64 rows whose
+// four waves share each tile through LDS (measured on the 70B batch against
+// two-chunk siblings: 6-, 8- and 16-token drafts 234 -> 202, 242 -> 215 and
+// 402 -> 366 us).  Int8 keys keep the siblings: in this scheme every wave
+// converts the whole key tile for its one chunk, which measured slower.
+template <class M, class Tr, int D, bool kShared, int kBS>
+hipError_t launch_lds_s(const DecodeArgs& a, int wgs, hipStream_t stream) {
+  const dim3 grid(a.num_kv_heads * wgs * a.num_seqs * a.num_parts);
+  hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, 1, kShared, kBS, false, true>), grid,
+                     dim3(4 * 64), 0, stream, a);
+  return hipGetLastError();
+}
+template <class M, class Tr, int D>
+hipError_t launch_lds(const DecodeArgs& a, hipStream_t stream) {
+  const int rows = a.num_query_tokens * (a.num_q_heads / a.num_kv_heads);
+  const int wgs = (rows + 63) / 64;
+  if (a.block_size == 8)
+    return wgs > 1 ? launch_lds_s<M, Tr, D, true, 8>(a, wgs, stream)
+                   : launch_lds_s<M, Tr, D, false, 8>(a, wgs, stream);
+  return wgs > 1 ? launch_lds_s<M, Tr, D, true, 16>(a, wgs, stream)
+                 : launch_lds_s<M, Tr, D, false, 16>(a, wgs, stream);
+}
+
 template <class M, class Tr, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (M::kKBytes == 2) {
+    if (a.num_query_tokens * (a.num_q_heads / a.num_kv_heads) > 32)
+      return launch_lds<M, Tr, D>(a, stream);
+  }
   if constexpr (M::kKBytes == 4 && D == 128) {
     // an 8 KiB float32 tile fills the registers already: one chunk per workgroup
     return launch_c<M, Tr, D, 1>(a, stream);

@@ -95,6 +95,7 @@ CASES = [
     ("f16", 128, 32, 32, 1, 32, False), ("f32", 64, 8, 2, 1, 0, False),
     ("bf16", 64, 16, 2, 3, 16, False), ("bf16", 128, 64, 8, 1, 0, True),
     ("f16", 128, 16, 2, 2, 48, True), ("f32", 128, 8, 4, 2, 16, False),
+    ("bf16", 128, 64, 8, 8, 0, False), ("f16", 64, 32, 4, 5, 32, False),
 ]
 
 

@@ -45,6 +45,9 @@ CASES = [
     ("bf16", 128, 16, 2, 5, 16), ("f16", 128, 8, 8, 4, 0), ("f16", 64, 16, 1, 3, 0),
     ("f16", 128, 32, 4, 8, 48), ("f32", 64, 8, 2, 4, 0), ("f32", 128, 8, 4, 2, 16),
     ("bf16", 64, 64, 1, 1, 0), ("bf16", 128, 128, 2, 1, 32), ("f32", 64, 4, 4, 6, 32),
+    # more than 32 rows per KV head: 64-row workgroups sharing tiles through LDS,
+    # one with a wave of padding rows (48), siblings with three (80)
+    ("bf16", 128, 64, 8, 6, 0), ("f16", 128, 16, 2, 10, 32), ("bf16", 64, 32, 4, 6, 16),
 ]
 
 
