@@ -813,8 +813,11 @@ hipError_t launch_c(const DecodeArgs& a, hipStream_t stream) {
 // More than 32 rows per KV head with 16-bit keys: workgroups of 64 rows whose
 // four waves share each tile through LDS (measured on the 70B batch against
 // two-chunk siblings: 6-, 8- and 16-token drafts 234 -> 202, 242 -> 215 and
-// 402 -> 366 us).  Int8 keys keep the siblings: in this scheme every wave
-// converts the whole key tile for its one chunk, which measured slower.
+// 402 -> 366 us).  Up to 32 rows one two-chunk workgroup per KV head stays:
+// with two of the four waves idle the LDS workgroup is no faster there and
+// varies from launch to launch.  Int8 keys keep the register path: in this
+// scheme every wave converts the whole key tile for its one chunk, which
+// measured slower.
 template <class M, class Tr, int D, bool kShared, int kBS>
 hipError_t launch_lds_s(const DecodeArgs& a, int wgs, hipStream_t stream) {
   const dim3 grid(a.num_kv_heads * wgs * a.num_seqs * a.num_parts);

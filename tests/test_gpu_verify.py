@@ -103,9 +103,22 @@ def test_verify_longest_draft(P):
     assert_close(widen_f32(out), want, TOL["bf16"], f"T{T} P{P}")
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,T,P", [("bf16", 64, 8, 4, 0), ("f16", 16, 2, 3, 32),
-                                              ("f32", 8, 2, 2, 0)])
-def test_verify_row_equals_sequential_decode(dtype, hq, hkv, T, P):
+# (dtype, H_q, H_kv, T, partition, same schedule).  With at most 32 rows per KV
+# head a verify call and a one-token decode run the same step schedule (the
+# waves of a workgroup deal the steps out alike whatever the chunk count), so
+# every row sees the same steps in the same waves and the outputs agree to the
+# rounding of the output.  With more rows and 16-bit keys the verify call shares
+# tiles through LDS, each wave walking every step of its rows: the online
+# softmax keeps other reference maxima, the weights round to the KV type
+# differently, and the two agree to the parity tolerance (both are within it
+# of the oracle).
+SEQ_CASES = [("bf16", 64, 8, 4, 0, True), ("f16", 16, 2, 3, 32, True), ("f32", 8, 2, 2, 0, True),
+             ("bf16", 64, 8, 6, 0, False), ("f16", 16, 2, 5, 32, False)]
+
+
+@pytest.mark.parametrize("case", range(len(SEQ_CASES)))
+def test_verify_row_equals_sequential_decode(case):
+    dtype, hq, hkv, T, P, same_schedule = SEQ_CASES[case]
     lens = [T, 20, 64, 100, 257]
     d = 128 if dtype != "f32" else 64
     w = wl.make_random_case(950, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
@@ -124,8 +137,11 @@ def test_verify_row_equals_sequential_decode(dtype, hq, hkv, T, P):
                                  lens_i, w.max_context_len, w.scale, partition_size=P)
         torch.cuda.synchronize()
         seq = widen_f32(one)
-        ulp = np.maximum(np.abs(seq), 2.0 ** -14) * 2.0 ** -ULP_BITS[dtype]
-        assert (np.abs(ver[:, i] - seq) <= ulp).all(), f"draft row {i}"
+        if same_schedule:
+            bound = np.maximum(np.abs(seq), 2.0 ** -14) * 2.0 ** -ULP_BITS[dtype]
+        else:
+            bound = TOL[dtype]
+        assert (np.abs(ver[:, i] - seq) <= bound).all(), f"draft row {i}"
 
 
 def test_verify_70b_gqa_4k_draft4_sampled():
