@@ -116,10 +116,62 @@ def _check(fn: str, status: int) -> None:
         raise PAError(fn, status)
 
 
-def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor | None = None) -> PoolDesc:
-    """Descriptor of a K pool tensor shaped [num_blocks][H_kv][d / x][16][x].  An
-    int8 K pool (quantised keys) takes its value type from ``v_pool``."""
+class _Args:
+    """Checks of the tensor arguments of one call: each one must be what the C
+    ABI reads through its pointer -- contiguous, of the element type and rank
+    given, with the sizes given (None = any) -- and, once all have passed,
+    every one must be on the GPU.  None and raw integer device addresses pass
+    unchecked.  A failure raises ValueError naming the call and the argument."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.tensors = []
+
+    def __call__(self, name: str, t, dtype=None, ndim: int | None = None, shape=None) -> None:
+        fn = self.fn
+        if t is None or isinstance(t, int):
+            return
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{fn}: {name} must be a tensor or a device address")
+        dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
+        if dtype is not None and t.dtype not in dtypes:
+            raise ValueError(f"{fn}: {name} is {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+        if ndim is not None and t.dim() != ndim:
+            raise ValueError(f"{fn}: {name} has {t.dim()} dimensions, expected {ndim}")
+        if shape is not None:
+            for i, want in enumerate(shape):
+                if want is not None and t.shape[i] != want:
+                    raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected size "
+                                     f"{want} in dimension {i}")
+        if not t.is_contiguous():
+            raise ValueError(f"{fn}: {name} must be contiguous")
+        self.tensors.append((name, t))
+
+    def on_gpu(self) -> None:
+        for name, t in self.tensors:
+            if not t.is_cuda:
+                raise ValueError(f"{self.fn}: {name} must be on the GPU")
+
+
+VALUE_TYPES = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _value_dtype(k_pool, v_pool):
+    """Element type of q, out, V and new K/V rows for this pool pair."""
+    return v_pool.dtype if v_pool is not None else k_pool.dtype
+
+
+def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor | None = None,
+              chk: _Args | None = None) -> PoolDesc:
+    """Descriptor of a K pool tensor shaped [num_blocks][H_kv][d / x][bs][x]
+    (with its V pool [num_blocks][H_kv][d][bs]).  An int8 K pool (quantised
+    keys) takes its value type from ``v_pool``."""
+    chk = chk or _Args("pool_desc")
+    chk("k_pool", k_pool, (torch.int8,) + VALUE_TYPES, 5)
     nb, hkv, nchunk, bs, x = k_pool.shape
+    if v_pool is not None:
+        want = VALUE_TYPES[1:] if k_pool.dtype == torch.int8 else k_pool.dtype
+        chk("v_pool", v_pool, want, 4, (nb, hkv, nchunk * x, bs))
     if k_pool.dtype == torch.int8:
         vt = None if v_pool is None else v_pool.dtype
         dt = {torch.float16: PA_K8_F16, torch.bfloat16: PA_K8_BF16}.get(vt, -1)
@@ -133,14 +185,21 @@ def pa_status_string(status: int) -> str:
 
 
 def pa_init_pool(k_pool, v_pool, fill: int = 0, stream=None) -> None:
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_init_pool")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk.on_gpu()
     _check("pa_init_pool", load().pa_init_pool(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
                                                fill, _stream(stream)))
 
 
 def pa_write_kv(k_pool, v_pool, k_new, v_new, slot_mapping, stream=None) -> None:
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_write_kv")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk("slot_mapping", slot_mapping, torch.int64, 1)
     n = int(slot_mapping.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        chk(name, t, v_pool.dtype, 3, (n, desc.num_kv_heads, desc.head_dim))
+    chk.on_gpu()
     _check("pa_write_kv", load().pa_write_kv(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
                                              _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), n,
                                              _stream(stream)))
@@ -152,11 +211,26 @@ def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
                                                 partition_size))
 
 
+def _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, workspace, out, ndim):
+    vt = _value_dtype(k_pool, v_pool)
+    chk("q", q, vt, ndim)
+    if q.shape[-1] != desc.head_dim:
+        raise ValueError(f"{chk.fn}: q has head_dim {q.shape[-1]}, the pool {desc.head_dim}")
+    B = int(q.shape[0])
+    chk("block_tables", block_tables, torch.int32, 2, (B, None))
+    chk("context_lens", context_lens, torch.int32, 1, (B,))
+    chk("workspace", workspace, torch.float32)
+    chk("out", out, vt, ndim, tuple(q.shape))
+
+
 def pa_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int, scale: float,
               partition_size: int = 0, workspace=None, out=None, stream=None) -> None:
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_decode")
+    desc = pool_desc(k_pool, v_pool, chk)
+    _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, workspace, out, 3)
     B, Hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    chk.on_gpu()
     _check("pa_decode", load().pa_decode(
         ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, Hq, int(max_context_len),
@@ -167,9 +241,12 @@ def pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_
                      scale: float, partition_size: int = 0, workspace=None, out=None,
                      stream=None) -> None:
     """q and out: [B][T][H_q][d] (T draft tokens per sequence)."""
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_verify_decode")
+    desc = pool_desc(k_pool, v_pool, chk)
+    _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, workspace, out, 4)
     B, T, Hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    chk.on_gpu()
     _check("pa_verify_decode", load().pa_verify_decode(
         ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq, int(max_context_len),
@@ -178,8 +255,14 @@ def pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_
 
 def pa_write_kv_k8(k_pool, v_pool, k_scale, k_new, v_new, slot_mapping, stream=None) -> None:
     """int8 key pool: k_new / v_new [T][H_kv][d] in the value type, k_scale float32 [H_kv][d]."""
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_write_kv_k8")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk("k_scale", k_scale, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
+    chk("slot_mapping", slot_mapping, torch.int64, 1)
     n = int(slot_mapping.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        chk(name, t, v_pool.dtype, 3, (n, desc.num_kv_heads, desc.head_dim))
+    chk.on_gpu()
     _check("pa_write_kv_k8", load().pa_write_kv_k8(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(k_new), _ptr(v_new),
         _ptr(slot_mapping), n, _stream(stream)))
@@ -189,9 +272,13 @@ def pa_decode_k8(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_con
                  scale: float, partition_size: int = 0, workspace=None, out=None,
                  stream=None) -> None:
     """q and out: [B][T][H_q][d] in the value type (T = 1: decode)."""
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_decode_k8")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk("k_scale", k_scale, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
+    _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, workspace, out, 4)
     B, T, Hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    chk.on_gpu()
     _check("pa_decode_k8", load().pa_decode_k8(
         ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq, int(max_context_len),
@@ -200,6 +287,14 @@ def pa_decode_k8(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_con
 
 def pa_reduce(workspace, context_lens, num_seqs: int, num_q_heads: int, head_dim: int,
               max_context_len: int, partition_size: int, out, stream=None) -> None:
+    chk = _Args("pa_reduce")
+    chk("workspace", workspace, torch.float32)
+    chk("context_lens", context_lens, torch.int32, 1, (num_seqs,))
+    chk("out", out, VALUE_TYPES)
+    if isinstance(out, torch.Tensor) and out.numel() != num_seqs * num_q_heads * head_dim:
+        raise ValueError(f"pa_reduce: out holds {out.numel()} elements, expected "
+                         f"{num_seqs} x {num_q_heads} x {head_dim}")
+    chk.on_gpu()
     _check("pa_reduce", load().pa_reduce(
         _ptr(workspace), _ptr(context_lens), num_seqs, num_q_heads, head_dim,
         int(max_context_len), int(partition_size), TORCH_TO_PA.get(out.dtype, -1), _ptr(out),
@@ -208,7 +303,12 @@ def pa_reduce(workspace, context_lens, num_seqs: int, num_q_heads: int, head_dim
 
 def pa_debug_slot_ids(block_tables, context_lens, max_context_len: int, num_blocks: int,
                       slot_ids, stream=None, block_size: int = BLOCK_SIZE) -> None:
+    chk = _Args("pa_debug_slot_ids")
+    chk("context_lens", context_lens, torch.int32, 1)
     B = int(context_lens.shape[0])
+    chk("block_tables", block_tables, torch.int32, 2, (B, None))
+    chk("slot_ids", slot_ids, torch.int64, 2, (B, int(max_context_len)))
+    chk.on_gpu()
     _check("pa_debug_slot_ids", load().pa_debug_slot_ids(
         _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B,
         int(max_context_len), int(num_blocks), int(block_size), _ptr(slot_ids), _stream(stream)))
@@ -216,21 +316,40 @@ def pa_debug_slot_ids(block_tables, context_lens, max_context_len: int, num_bloc
 
 def pa_copy_blocks(k_pool, v_pool, src_dst, stream=None) -> None:
     """src_dst: int32 device tensor [n][2] of (source, destination) blocks."""
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_copy_blocks")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk("src_dst", src_dst, torch.int32, 2, (None, 2))
     n = int(src_dst.shape[0]) if src_dst is not None else 0
+    chk.on_gpu()
     _check("pa_copy_blocks", load().pa_copy_blocks(ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool),
                                                    _ptr(src_dst), n, _stream(stream)))
 
 
+def _staging_args(chk, k_pool, v_pool, block_ids, k_buf, v_buf):
+    chk("block_ids", block_ids, torch.int32, 1)
+    n = int(block_ids.shape[0])
+    for name, t, pool in (("k", k_buf, k_pool), ("v", v_buf, v_pool)):
+        chk(name, t, pool.dtype)
+        if isinstance(t, torch.Tensor) and t.numel() < n * (pool.numel() // pool.shape[0]):
+            raise ValueError(f"{chk.fn}: {name} holds {t.numel()} elements, {n} blocks need "
+                             f"{n * (pool.numel() // pool.shape[0])}")
+
+
 def pa_gather_blocks(k_pool, v_pool, block_ids, k_dst, v_dst, stream=None) -> None:
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_gather_blocks")
+    desc = pool_desc(k_pool, v_pool, chk)
+    _staging_args(chk, k_pool, v_pool, block_ids, k_dst, v_dst)
+    chk.on_gpu()
     _check("pa_gather_blocks", load().pa_gather_blocks(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
         _ptr(k_dst), _ptr(v_dst), _stream(stream)))
 
 
 def pa_scatter_blocks(k_pool, v_pool, block_ids, k_src, v_src, stream=None) -> None:
-    desc = pool_desc(k_pool, v_pool)
+    chk = _Args("pa_scatter_blocks")
+    desc = pool_desc(k_pool, v_pool, chk)
+    _staging_args(chk, k_pool, v_pool, block_ids, k_src, v_src)
+    chk.on_gpu()
     _check("pa_scatter_blocks", load().pa_scatter_blocks(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
         _ptr(k_src), _ptr(v_src), _stream(stream)))

@@ -113,9 +113,9 @@ def test_slot_ids_bit_exact(i):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", wl.DTYPES)
 def test_init_pool(dtype):
-    ks, _ = wl.pool_shapes(5, 2, 64, dtype)
+    ks, vs = wl.pool_shapes(5, 2, 64, dtype)
     kp = torch.full(ks, 3.0, dtype=TORCH_DTYPE[dtype], device=DEV)
-    vp = kp.clone()
+    vp = torch.full(vs, 3.0, dtype=TORCH_DTYPE[dtype], device=DEV)
     pa.pa_init_pool(kp, vp, 1)
     torch.cuda.synchronize()
     assert torch.isnan(kp).all() and torch.isnan(vp).all()
