@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   const int blk_hi = t_hi > t_lo ? (t_hi + kStep - 1) / kStep : blk_lo;
   // Query token i sees the tokens [0, L - T + 1 + i) (the draft is causal; one
   // query token sees the whole context).  Blocks that end past the smallest
-  // limit of this workgroup's rows are masked row by row.
+  // limit of this wave's rows are masked row by row.
   const int t_hi_min = min(t_hi, L - T + 1 + row0 / group);
 
   // Per chunk c, lane l holds row row0 + 16 c + r: the B operands of its logits
