@@ -162,7 +162,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              f"(the decode path is single-GPU; see DESIGN.md for how it would shard)",
+              f"(the decode path is single-GPU; split by sequence or KV head it needs no exchange)",
               file=sys.stderr)
         return 2
 

@@ -22,7 +22,7 @@ method's fast form.  The pages it follows (cited by title and section):
        §3.2 block-table figure (block i holds tokens 16i..16i+15, logical
        blocks 0/1/2 map to physical #7/#2/#11); §4.2 online softmax is exact.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * GQA grouping is contiguous: q-head h reads KV head h // (H_q / H_kv).
 * A context of length 0 attends to nothing: the output row is 0 and every

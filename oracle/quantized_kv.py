@@ -15,7 +15,7 @@ What it follows (cited by title and section):
   channel's scale from the maximum magnitude over the token axis and stores
   round(k / scale) clamped to the signed range.
 
-Readings (each listed in the design doc):
+Readings (where the pages leave a step open):
 
 * Symmetric int8 per channel: scale_c = amax_c / 127, code = clamp(rint(k /
   scale_c), -127, 127), k_hat = code * scale_c.  The printed sketch divides the
