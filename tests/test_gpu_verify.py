@@ -48,6 +48,8 @@ CASES = [
     # more than 32 rows per KV head: 64-row workgroups sharing tiles through LDS,
     # one with a wave of padding rows (48), siblings with three (80)
     ("bf16", 128, 64, 8, 6, 0), ("f16", 128, 16, 2, 10, 32), ("bf16", 64, 32, 4, 6, 16),
+    # float32 keys past 32 rows: sibling workgroups (one chunk at d 128, two at d 64)
+    ("f32", 128, 16, 2, 5, 0), ("f32", 64, 32, 2, 3, 16),
 ]
 
 
