@@ -317,6 +317,41 @@ def test_single_token_context_returns_v0_exactly(dtype):
             assert np.array_equal(out[s, h].view(np.uint8), want.view(np.uint8))
 
 
+@pytest.mark.parametrize("P", [0, 32])
+def test_out_of_range_device_data_is_clamped(P):
+    """Device data are not validated; the header states what the kernels read
+    instead: a physical id outside the pool is clamped into it, a context length
+    into [0, max_context_len].  Out-of-range entries must give exactly the result
+    of the clamped table and lengths (and gather indices bit for bit)."""
+    lens = [40, 100, 300, 77]
+    w = wl.make_random_case(1300, num_seqs=4, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                            dtype="bf16", lens=lens)
+    rng = np.random.default_rng(1301)
+    nb = w.num_blocks
+    for b in (0, nb - 1):  # the blocks the clamped ids land on hold finite data
+        w.k_pool[b] = wl.normal(rng, w.k_pool.shape[1:], "bf16")
+        w.v_pool[b] = wl.normal(rng, w.v_pool.shape[1:], "bf16")
+    bad_tables = w.block_tables.copy()
+    bad_tables[0, 1] = nb + 5   # past the pool
+    bad_tables[1, 0] = -3       # negative
+    bad_lens = np.array([40, 100, 1000, -7], np.int32)   # past max_context_len (300), negative
+    tables = bad_tables.copy()
+    tables[0, 1], tables[1, 0] = nb - 1, 0
+    clamped = np.array([40, 100, 300, 0], np.int32)
+    d = upload(w, DEV)
+    d.block_tables = torch.from_numpy(bad_tables).to(DEV)
+    d.context_lens = torch.from_numpy(bad_lens).to(DEV)
+    got = widen_f32(run_decode(d, P)[0])
+    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, tables, clamped, w.scale, "bf16")
+    assert_close(got, want, TOL["bf16"], f"clamped P{P}")
+    assert not got[3].any()
+    out = torch.empty((4, w.max_context_len), dtype=torch.int64, device=DEV)
+    pa.pa_debug_slot_ids(d.block_tables, d.context_lens, w.max_context_len, nb, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(),
+                          oracle.slot_ids(tables, clamped, w.max_context_len, 16))
+
+
 def test_uniform_v_and_poisoned_slots():
     kw = dict(num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="bf16",
               lens=[5, 16, 47, 129])
