@@ -109,9 +109,21 @@ QK_MUTATIONS = {
     "clamp_128": ("np.clip(np.rint(quotient), -K8_MAX, K8_MAX)", "np.clip(np.rint(quotient), -K8_MAX - 1, K8_MAX)"),
     "multiply_by_scale": ("quotient = kf / np.asarray(k_scale, dtype=np.float32)",
                           "quotient = kf * np.asarray(k_scale, dtype=np.float32)"),
-    "first_head_scales": ("K = dequantize_k(k_rows(k8_pool, block_tables[s], L, g), k_scale[g])\n            V = widen(v_rows(v_pool, block_tables[s], L, g), dtype)\n            for i in range(T):\n                lim = draft_limit(L, T, i)\n                for h in range(Hq):",
-                          "K = dequantize_k(k_rows(k8_pool, block_tables[s], L, g), k_scale[0])\n            V = widen(v_rows(v_pool, block_tables[s], L, g), dtype)\n            for i in range(T):\n                lim = draft_limit(L, T, i)\n                for h in range(Hq):"),
+    "first_head_scales": ("keys = lambda s, g, L: dequantize_k(k_rows(k8_pool, block_tables[s], L, g), k_scale[g])\n    return _decode_over_keys",
+                          "keys = lambda s, g, L: dequantize_k(k_rows(k8_pool, block_tables[s], L, g), k_scale[0])\n    return _decode_over_keys"),
     "write_v_as_k": ("                v_out[b, g, c, o] = v_new[i, g, c]", "                v_out[b, g, c, o] = k_new[i, g, c]"),
+    # 2-bit keys
+    "k2_no_zero_point": ("return z + s * codes.astype(np.float64)", "return s * codes.astype(np.float64)"),
+    "k2_truncate": ("return np.rint(u).astype(np.uint8)", "return np.trunc(u).astype(np.uint8)"),
+    "k2_symmetric_steps": ("np.float32(K2_STEPS))  # fmax/fmin", "np.float32(K2_STEPS + 1))  # fmax/fmin"),
+    "k2_zero_added": ("u = (kf - np.asarray(k_zero, np.float32))", "u = (kf + np.asarray(k_zero, np.float32))"),
+    "k2_half_swap": ("(c % 8) // 2) + 16 * (c % 2)", "(c % 8) // 2) + 16 * ((c // 2) % 2)"),
+    "k2_step_order": ("c // 64, 2 * (4 * ((c // 32) % 2)", "c // 64, 2 * (4 * ((c // 64) % 2)"),
+    "k2_group_of_channel": ("return (c % 32) // 8, c // 64", "return (c % 64) // 16, c // 64"),
+    "k2_token_offset": ("offset = t % bs\n    rows = np.empty((length, d), np.uint8)",
+                        "offset = (t + 1) % bs\n    rows = np.empty((length, d), np.uint8)"),
+    "k2_first_head_zero": ("k_scale[g],\n                                         k_zero[g])\n    return _partials_over_keys",
+                           "k_scale[g],\n                                         k_zero[0])\n    return _partials_over_keys"),
 }
 
 
@@ -125,6 +137,6 @@ def test_planted_quantized_kv_mistake_is_caught(name, tmp_path):
                         ignore=shutil.ignore_patterns("__pycache__", "*.so", "csrc"))
     (tmp_path / "oracle" / "quantized_kv.py").write_text(source.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_quantized_kv_pins.py"], cwd=tmp_path, capture_output=True,
+                        "tests/test_quantized_kv_pins.py", "tests/test_quantized_k2_pins.py"], cwd=tmp_path, capture_output=True,
                        text=True, timeout=300)
     assert r.returncode != 0, f"no pin caught the planted mistake {name}:\n{r.stdout[-2000:]}"
