@@ -72,18 +72,19 @@ def decode_kernel_bytes(w, partition: int, query_tokens: int = 1, key_bytes=None
     e = ELEM_BYTES[w.dtype]
     live = int(((w.context_lens.astype("int64") + 15) // 16).sum())
     qo = query_tokens * w.num_seqs * w.num_q_heads * w.head_dim * e
-    scales = 4 * w.num_kv_heads * w.head_dim if key_bytes == 1 else 0
+    scales = {1: 4, 0.25: 8}.get(key_bytes, 0) * w.num_kv_heads * w.head_dim
     return (w.kv_bytes_logical(key_bytes) + qo * (1 if partition else 2) + 4 * live +
             4 * w.num_seqs + scales)
 
 
 def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0, verify_q=None,
-                 k8=None):
+                 k8=None, k2=None):
     """The fp64 oracle, single-threaded, on the same workload: whole passes over
     every sequence until about ``min_seconds`` have elapsed (bounded by
     ``max_seconds``; the last pass may stop early).  ``verify_q`` [B][T][H_q][d]:
     time the verify oracle over that draft instead; ``k8`` = (codes, scales):
-    the int8-key oracle."""
+    the int8-key oracle; ``k2`` = (words, steps, zero points): the 2-bit-key
+    oracle."""
     import oracle
     from oracle import quantized_kv
     from threadpoolctl import threadpool_limits
@@ -93,7 +94,12 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0, verify
         done_seqs = 0
         while time.perf_counter() - t0 < min_seconds:
             for s in range(B):
-                if k8 is not None:
+                if k2 is not None:
+                    qs = w.q[s:s + 1, None] if verify_q is None else verify_q[s:s + 1]
+                    quantized_kv.paged_decode_k2(qs, k2[0], w.v_pool, w.block_tables[s:s + 1],
+                                                 w.context_lens[s:s + 1], w.scale, k2[1], k2[2],
+                                                 w.dtype)
+                elif k8 is not None:
                     qs = w.q[s:s + 1, None] if verify_q is None else verify_q[s:s + 1]
                     quantized_kv.paged_decode_k8(qs, k8[0], w.v_pool, w.block_tables[s:s + 1],
                                                  w.context_lens[s:s + 1], w.scale, k8[1], w.dtype)
@@ -110,7 +116,8 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0, verify
         dt = time.perf_counter() - t0
     frac = done_seqs / B
     T = 1 if verify_q is None else verify_q.shape[1]
-    gbps = w.algorithmic_bytes(query_tokens=T, key_bytes=1 if k8 is not None else None) * frac / dt / 1e9
+    key_bytes = 1 if k8 is not None else (0.25 if k2 is not None else None)
+    gbps = w.algorithmic_bytes(query_tokens=T, key_bytes=key_bytes) * frac / dt / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done_seqs} sequences ({frac:.2f} passes over all {B} sequences x "
                       f"{w.num_q_heads} heads of the workload), numpy float64, one thread, "
@@ -149,8 +156,9 @@ def main() -> int:
     ap.add_argument("--longest-first", action="store_true",
                     help="order the batch by context length, longest first, as a scheduler "
                          "would with pa_bm_sort_longest_first (the workload is otherwise as drawn)")
-    ap.add_argument("--kv", choices=("native", "k8"), default="native",
-                    help="k8: int8 keys with per-channel scales (pa_decode_k8), values in the "
+    ap.add_argument("--kv", choices=("native", "k8", "k2"), default="native",
+                    help="k8: int8 keys with per-channel scales (pa_decode_k8); k2: 2-bit keys "
+                         "with per-channel steps and zero points (pa_decode_k2); values in the "
                          "workload's 16-bit type")
     ap.add_argument("--verify", type=int, default=0, metavar="T",
                     help="time the speculative-decoding verify call over a T-token draft "
@@ -190,16 +198,23 @@ def main() -> int:
     T = max(args.verify, 1)
     B, Hq, D = d.q.shape
     k8 = args.kv == "k8"
-    key_bytes = 1 if k8 else None
+    k2 = args.kv == "k2"
+    key_bytes = 1 if k8 else (0.25 if k2 else None)
+    if (k8 or k2) and w.dtype not in ("f16", "bf16"):
+        print(f"--kv {args.kv} needs a 16-bit workload", file=sys.stderr)
+        return 2
+    if k2:
+        words, k2_step, k2_zero = wl.k2_inputs(w, 4343 + args.config,
+                                               outlier_columns=10 if args.config == 2 else 0)
+        k2_pool = torch.from_numpy(words.view(np.int32)).to("cuda")
+        k2_step_t = torch.from_numpy(k2_step).to("cuda")
+        k2_zero_t = torch.from_numpy(k2_zero).to("cuda")
     if k8:
-        if w.dtype not in ("f16", "bf16"):
-            print("--kv k8 needs a 16-bit workload", file=sys.stderr)
-            return 2
         codes, kscale = wl.k8_inputs(w, 4242 + args.config,
                                      outlier_columns=10 if args.config == 2 else 0)
         k8_pool = torch.from_numpy(codes).to("cuda")
         k8_scale = torch.from_numpy(kscale).to("cuda")
-    if args.verify or k8:
+    if args.verify or k8 or k2:
         from paged_kv_cache_365_amd.device import to_torch
         q_np = wl.normal(np.random.default_rng(7), (B, T, Hq, D), w.dtype)
         qv = to_torch(q_np, w.dtype, "cuda")
@@ -225,7 +240,11 @@ def main() -> int:
         after reduce)."""
         if ev is not None:
             ev[0].record(stream)
-        if k8:
+        if k2:
+            pa.pa_decode_k2(qv, k2_pool, d.v_pool, k2_step_t, k2_zero_t, d.block_tables,
+                            d.context_lens, d.max_context_len, d.scale, P, ws, None if P else out,
+                            stream)
+        elif k8:
             pa.pa_decode_k8(qv, k8_pool, d.v_pool, k8_scale, d.block_tables, d.context_lens,
                             d.max_context_len, d.scale, P, ws, None if P else out, stream)
         elif args.verify:
@@ -285,7 +304,8 @@ def main() -> int:
     value = alg / (ms_per_step * 1e-3) / 1e9
     kbytes = decode_kernel_bytes(w, P, T, key_bytes)
     achieved = kbytes / (decode_ms * 1e-3) / 1e9
-    workload = w.name + ("-k8" if k8 else "") + (f"-verify{T}" if args.verify else "")
+    workload = (w.name + ("-k8" if k8 else "") + ("-k2" if k2 else "") +
+                (f"-verify{T}" if args.verify else ""))
     traffic = stored_traffic(workload, P)
 
     rec = {
@@ -299,7 +319,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"i8k-{w.dtype}" if k8 else w.dtype,
+        "dtype": f"i8k-{w.dtype}" if k8 else (f"u2k-{w.dtype}" if k2 else w.dtype),
         "accum_dtype": "f32",
         "data": "synthetic",
         "config": {
@@ -315,7 +335,8 @@ def main() -> int:
         "decode_us": round(decode_ms * 1e3, 2),
         "reduce_us": round(reduce_ms * 1e3, 2),
         "roofline": {
-            "kernel": "pa_decode_k8" if k8 else ("pa_verify_decode" if args.verify else "pa_decode"),
+            "kernel": ("pa_decode_k8" if k8 else "pa_decode_k2" if k2 else
+                       "pa_verify_decode" if args.verify else "pa_decode"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -333,7 +354,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host (cpu_baseline)")
         rec["cpu_baseline"] = cpu_baseline(w, verify_q=q_np if args.verify else None,
-                                           k8=(codes, kscale) if k8 else None)
+                                           k8=(codes, kscale) if k8 else None,
+                                           k2=(words, k2_step, k2_zero) if k2 else None)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

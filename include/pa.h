@@ -24,6 +24,7 @@
  *  - Element dtype: PA_F32 (IEEE binary32), PA_F16 (IEEE binary16), PA_BF16
  *    (bfloat16).  q, out, the pools and new K/V rows share the pool dtype.
  *    PA_K8_F16 / PA_K8_BF16: int8 keys (see pa_write_kv_k8), 16-bit values.
+ *    PA_K2_F16 / PA_K2_BF16: 2-bit keys (see pa_write_kv_k2), 16-bit values.
  *  - KV pool layout.  Both pools are arrays of tiles, one tile per (physical
  *    block, kv head), block-major then head; a tile holds the bs tokens of the
  *    block (bs = block_size, 16 or 8), bs * head_dim elements, contiguous (4 KiB
@@ -39,6 +40,14 @@
  *    contiguous per-lane load.  An int8 key pool (PA_K8_*) has the same K
  *    order with x = 16: [num_blocks][num_kv_heads][head_dim / 16][16][16]
  *    (2 KiB tiles of 16 tokens at head_dim 128); its V pool is the 16-bit one.
+ *    A 2-bit key pool (PA_K2_*) holds bs * head_dim / 16 32-bit words per tile
+ *    (512 bytes for 16 tokens at head_dim 128), as uint32
+ *    [num_blocks][num_kv_heads][4][bs][head_dim / 64]: channel c of the token
+ *    at offset o is the 2-bit field at bit 2 * (4 * ((c / 32) % 2) + (c % 8) / 2)
+ *    + 16 * (c % 2) of word [(c % 32) / 8][o][c / 64].  So word w of group q
+ *    holds channels 32 j + 8 q + e of one token for j = 2w, 2w + 1 and e = 0..7,
+ *    the two of a pair (e = 2i, 2i + 1) 16 bits apart: one shift and one mask
+ *    give the pair as the low bits of two 16-bit halves.
  *  - Block tables: int32 [num_seqs][max_blocks_per_seq], row-major.  Entry j of
  *    row s is the physical block of tokens bs*j .. bs*j + bs-1 of sequence s.
  *    Only the first ceil(context_lens[s] / bs) entries of a row are read.
@@ -78,7 +87,11 @@ typedef enum pa_dtype {
    * q and out are 16-bit (f16 or bf16).  Used by pa_write_kv_k8 and
    * pa_decode_k8; the plain pa_write_kv / pa_decode calls reject them. */
   PA_K8_F16 = 3,
-  PA_K8_BF16 = 4
+  PA_K8_BF16 = 4,
+  /* 2-bit keys with float32 per-(KV head, channel) scales and zero points, V,
+   * q and out 16-bit.  Used by pa_write_kv_k2 and pa_decode_k2 only. */
+  PA_K2_F16 = 5,
+  PA_K2_BF16 = 6
 } pa_dtype;
 
 /* Host-side description of a KV pool.  block_size is 16 (the pages' default)
@@ -94,7 +107,8 @@ typedef struct pa_pool_desc {
 
 /* Fill every element of both pools: fill = 0 writes +0.0, fill = 1 writes a
  * quiet NaN (used to prove that unreferenced blocks are never read; an int8
- * key pool gets -128, a code no write produces).  A pool
+ * key pool gets -128, a code no write produces; a 2-bit key pool, where every
+ * bit pattern is a code, gets all ones, code 3).  A pool
  * that has just been taken from the allocator (the fixed-capacity block pool of
  * §2.3 of the tanteng.space page). */
 pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int32_t fill,
@@ -219,6 +233,38 @@ pa_status pa_decode_k8(const pa_pool_desc* pool, const void* q, const void* k_po
                        float scale, int32_t partition_size, void* workspace,
                        size_t workspace_bytes, void* out, hipStream_t stream);
 
+/* 2-bit key cache, asymmetric per channel (KIVI as §4.2 of the
+ * blog.tanteng.space page describes it: keys at 2 bits per channel, values kept
+ * in 16-bit; asymmetric quantisation as "KV Cache量化" of the ybb.press page
+ * says).  The pool dtype is PA_K2_F16 or PA_K2_BF16.  k_scale and k_zero are
+ * float32 [num_kv_heads][head_dim] in device memory, 16-byte aligned: the
+ * static step s and zero point z of each key channel (e.g. a calibrated
+ * minimum z and s = (maximum - minimum) / 3), finite, s >= 0.
+ *
+ * pa_write_kv_k2: as pa_write_kv, but each key element k of channel c becomes
+ *   u = (k - z) / s  (float32 subtraction and division, round to nearest),
+ *   code = rint(min(max(u, 0), 3))  (ties to even; min/max ignore a NaN, so
+ *   s = 0 gives code 0 at or below z and 3 above it),
+ * stored in the 2-bit layout above (a written token's key words are replaced
+ * whole); V rows are copied bit for bit.  k_new and v_new are
+ * [num_tokens][H_kv][d] in the 16-bit type; key rows must be finite.
+ *
+ * pa_decode_k2: pa_verify_decode (num_query_tokens = 1 is pa_decode) over the
+ * dequantised keys z + s * code; q and out in the 16-bit type, split mode and
+ * pa_reduce as there (partials include the zero points' contribution to the
+ * log-sum-exp).  A K tile is 1/8 of a 16-bit one: 9/16 of the KV traffic per
+ * token. */
+pa_status pa_write_kv_k2(const pa_pool_desc* pool, void* k_pool, void* v_pool, const float* k_scale,
+                         const float* k_zero, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
+pa_status pa_decode_k2(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                       const void* v_pool, const float* k_scale, const float* k_zero,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_query_tokens,
+                       int32_t num_q_heads, int32_t max_context_len, float scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* out,
+                       hipStream_t stream);
+
 /* Copy whole blocks inside the pool: for each i < num_pairs, block
  * src_dst[2i + 1] of both pools becomes a copy of block src_dst[2i] (every KV
  * head, K and V).  This is the copy of a copy-on-write (§2.3 (2) of the
@@ -235,7 +281,7 @@ pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
  * pa_gather_blocks packs blocks block_ids[0 .. n) of both pools contiguously:
  * block i goes to k_dst / v_dst at byte offset i * block_bytes, block_bytes =
  * num_kv_heads * bs * head_dim * element size of that pool (the pool's own
- * tile order; 1 byte for int8 keys).
+ * tile order; 1 byte for int8 keys, 1/4 byte for 2-bit keys).
  * pa_scatter_blocks is the inverse: k_src / v_src block i goes to pool block
  * block_ids[i].  block_ids is int32 in device memory; ids outside the pool are
  * skipped.  The packed buffers must be device-accessible (device memory, or

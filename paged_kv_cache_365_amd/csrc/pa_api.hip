@@ -18,15 +18,19 @@ int elem_bytes(int32_t dtype) {
     case PA_F16:
     case PA_BF16:
     case PA_K8_F16:
-    case PA_K8_BF16: return 2;
+    case PA_K8_BF16:
+    case PA_K2_F16:
+    case PA_K2_BF16: return 2;
     default: return 0;
   }
 }
 
 bool is_k8(int32_t dtype) { return dtype == PA_K8_F16 || dtype == PA_K8_BF16; }
+bool is_k2(int32_t dtype) { return dtype == PA_K2_F16 || dtype == PA_K2_BF16; }
+bool is_quantized(int32_t dtype) { return is_k8(dtype) || is_k2(dtype); }
 
-// bytes of one K element in the pool
-int k_elem_bytes(int32_t dtype) { return is_k8(dtype) ? 1 : elem_bytes(dtype); }
+// bits of one K element in the pool
+int k_elem_bits(int32_t dtype) { return is_k2(dtype) ? 2 : (is_k8(dtype) ? 8 : 8 * elem_bytes(dtype)); }
 
 pa_status check_pool(const pa_pool_desc* pool) {
   if (!pool) return PA_ERR_INVALID_ARG;
@@ -40,9 +44,11 @@ pa_status check_pool(const pa_pool_desc* pool) {
 size_t block_elems(const pa_pool_desc* pool) {
   return static_cast<size_t>(pool->num_kv_heads) * pool->block_size * pool->head_dim;
 }
-size_t k_pool_bytes(const pa_pool_desc* pool) {
-  return pool->num_blocks * block_elems(pool) * k_elem_bytes(pool->dtype);
+// bytes of one block of the K pool (every KV head): a multiple of 16
+size_t k_block_bytes(const pa_pool_desc* pool) {
+  return block_elems(pool) * k_elem_bits(pool->dtype) / 8;
 }
+size_t k_pool_bytes(const pa_pool_desc* pool) { return pool->num_blocks * k_block_bytes(pool); }
 size_t v_pool_bytes(const pa_pool_desc* pool) {
   return pool->num_blocks * block_elems(pool) * elem_bytes(pool->dtype);
 }
@@ -79,9 +85,10 @@ pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return PA_ERR_MISALIGNED;
   uint32_t v_pattern = 0u, k_pattern = 0u;
   if (fill == 1) {
-    const bool f16 = pool->dtype == PA_F16 || pool->dtype == PA_K8_F16;
+    const bool f16 = pool->dtype == PA_F16 || pool->dtype == PA_K8_F16 || pool->dtype == PA_K2_F16;
     v_pattern = pool->dtype == PA_F32 ? 0x7FC00000u : (f16 ? 0x7E007E00u : 0x7FC07FC0u);
     k_pattern = is_k8(pool->dtype) ? 0x80808080u : v_pattern;  // int8 -128: no write makes it
+    if (is_k2(pool->dtype)) k_pattern = 0xFFFFFFFFu;  // every 2-bit pattern is a code: all 3s
   }
   hipError_t e = pa::launch_fill(k_pool, k_pool_bytes(pool), k_pattern, stream);
   if (e == hipSuccess) e = pa::launch_fill(v_pool, v_pool_bytes(pool), v_pattern, stream);
@@ -93,7 +100,7 @@ pa_status pa_write_kv(const pa_pool_desc* pool, void* k_pool, void* v_pool, cons
                       hipStream_t stream) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
-  if (is_k8(pool->dtype)) return PA_ERR_UNSUPPORTED;  // needs the key scales: pa_write_kv_k8
+  if (is_quantized(pool->dtype)) return PA_ERR_UNSUPPORTED;  // pa_write_kv_k8 / pa_write_kv_k2
   if (num_tokens < 0) return PA_ERR_INVALID_ARG;
   if (num_tokens == 0) return PA_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
@@ -122,7 +129,7 @@ namespace {
 
 // pa_decode and pa_verify_decode: T query tokens per sequence (T = 1: decode).
 pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_pool,
-                        const void* v_pool, const float* k_scale,
+                        const void* v_pool, const float* k_scale, const float* k_zero,
                         const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_query_tokens,
                         int32_t num_q_heads, int32_t max_context_len, float scale,
@@ -131,9 +138,10 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
-  if (is_k8(pool->dtype) != (k_scale != nullptr)) {
-    // int8 keys need their scales; other pools take none
-    return is_k8(pool->dtype) ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED;
+  if (is_quantized(pool->dtype) != (k_scale != nullptr) || is_k2(pool->dtype) != (k_zero != nullptr)) {
+    // quantised keys need their scales (2-bit keys their zero points too);
+    // other pools take none
+    return is_quantized(pool->dtype) ? PA_ERR_INVALID_ARG : PA_ERR_UNSUPPORTED;
   }
   if (num_seqs <= 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARG;
@@ -149,7 +157,7 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
   if (static_cast<int64_t>(num_seqs) * pool->num_kv_heads * ((rows + 15) / 16) * parts > INT32_MAX)
     return PA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(block_tables, 4) ||
-      !aligned(context_lens, 4) || !aligned(k_scale, 16))
+      !aligned(context_lens, 4) || !aligned(k_scale, 16) || !aligned(k_zero, 16))
     return PA_ERR_MISALIGNED;
 
   pa::DecodeArgs a{};
@@ -157,6 +165,7 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.k_scale = k_scale;
+  a.k_zero = k_zero;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.max_blocks_per_seq = max_blocks_per_seq;
@@ -206,8 +215,8 @@ pa_status pa_decode(const pa_pool_desc* pool, const void* q, const void* k_pool,
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
                     int32_t max_context_len, float scale, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, void* out, hipStream_t stream) {
-  if (pool && is_k8(pool->dtype)) return PA_ERR_UNSUPPORTED;  // pa_decode_k8
-  return decode_common(pool, q, k_pool, v_pool, nullptr, block_tables, max_blocks_per_seq,
+  if (pool && is_quantized(pool->dtype)) return PA_ERR_UNSUPPORTED;  // pa_decode_k8 / _k2
+  return decode_common(pool, q, k_pool, v_pool, nullptr, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, 1, num_q_heads, max_context_len, scale,
                        partition_size, workspace, workspace_bytes, out, stream);
 }
@@ -219,8 +228,8 @@ pa_status pa_verify_decode(const pa_pool_desc* pool, const void* q, const void* 
                            int32_t max_context_len, float scale, int32_t partition_size,
                            void* workspace, size_t workspace_bytes, void* out,
                            hipStream_t stream) {
-  if (pool && is_k8(pool->dtype)) return PA_ERR_UNSUPPORTED;  // pa_decode_k8
-  return decode_common(pool, q, k_pool, v_pool, nullptr, block_tables, max_blocks_per_seq,
+  if (pool && is_quantized(pool->dtype)) return PA_ERR_UNSUPPORTED;  // pa_decode_k8 / _k2
+  return decode_common(pool, q, k_pool, v_pool, nullptr, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_query_tokens, num_q_heads, max_context_len,
                        scale, partition_size, workspace, workspace_bytes, out, stream);
 }
@@ -233,7 +242,7 @@ pa_status pa_decode_k8(const pa_pool_desc* pool, const void* q, const void* k_po
                        size_t workspace_bytes, void* out, hipStream_t stream) {
   if (pool && !is_k8(pool->dtype)) return PA_ERR_UNSUPPORTED;  // pa_decode / pa_verify_decode
   if (!k_scale) return PA_ERR_INVALID_ARG;
-  return decode_common(pool, q, k_pool, v_pool, k_scale, block_tables, max_blocks_per_seq,
+  return decode_common(pool, q, k_pool, v_pool, k_scale, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_query_tokens, num_q_heads, max_context_len,
                        scale, partition_size, workspace, workspace_bytes, out, stream);
 }
@@ -255,6 +264,39 @@ pa_status pa_write_kv_k8(const pa_pool_desc* pool, void* k_pool, void* v_pool, c
                                          pool->num_kv_heads, pool->head_dim, pool->dtype, stream));
 }
 
+pa_status pa_decode_k2(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                       const void* v_pool, const float* k_scale, const float* k_zero,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_query_tokens,
+                       int32_t num_q_heads, int32_t max_context_len, float scale,
+                       int32_t partition_size, void* workspace, size_t workspace_bytes, void* out,
+                       hipStream_t stream) {
+  if (pool && !is_k2(pool->dtype)) return PA_ERR_UNSUPPORTED;  // pa_decode / _k8 / verify
+  if (!k_scale || !k_zero) return PA_ERR_INVALID_ARG;
+  return decode_common(pool, q, k_pool, v_pool, k_scale, k_zero, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_query_tokens, num_q_heads, max_context_len,
+                       scale, partition_size, workspace, workspace_bytes, out, stream);
+}
+
+pa_status pa_write_kv_k2(const pa_pool_desc* pool, void* k_pool, void* v_pool, const float* k_scale,
+                         const float* k_zero, const void* k_new, const void* v_new,
+                         const int64_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (!is_k2(pool->dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_scale || !k_zero || !k_new || !v_new || !slot_mapping)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+      !aligned(slot_mapping, 8) || !aligned(k_scale, 16) || !aligned(k_zero, 16))
+    return PA_ERR_MISALIGNED;
+  return from_hip(pa::launch_write_kv_k2(k_pool, v_pool, k_scale, k_zero, k_new, v_new,
+                                         slot_mapping, num_tokens, pool->num_blocks,
+                                         pool->block_size, pool->num_kv_heads, pool->head_dim,
+                                         pool->dtype, stream));
+}
+
 pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                     int32_t partition_size, int32_t out_dtype, void* out, hipStream_t stream) {
@@ -262,7 +304,7 @@ pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t 
   if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
   if (partition_size <= 0 || partition_size % pa::kStep != 0) return PA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
-  if (elem_bytes(out_dtype) == 0 || is_k8(out_dtype)) return PA_ERR_UNSUPPORTED;
+  if (elem_bytes(out_dtype) == 0 || is_quantized(out_dtype)) return PA_ERR_UNSUPPORTED;
   if (!aligned(workspace, 16) || !aligned(out, 16) || !aligned(context_lens, 4))
     return PA_ERR_MISALIGNED;
   // one 64-lane wavefront per 32 output columns of a row: the threads must fit a 1-D grid
@@ -304,7 +346,7 @@ pa_status pa_copy_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
   a.dst_stride = 2;
   a.dst_limit = pool->num_blocks;
   a.num_pairs = num_pairs;
-  a.k_block_bytes = block_elems(pool) * k_elem_bytes(pool->dtype);
+  a.k_block_bytes = k_block_bytes(pool);
   a.v_block_bytes = block_elems(pool) * elem_bytes(pool->dtype);
   a.skip_equal = true;
   return from_hip(pa::launch_block_move(a, stream));
@@ -333,7 +375,7 @@ pa_status pa_gather_blocks(const pa_pool_desc* pool, const void* k_pool, const v
   a.dst_stride = 1;
   a.dst_limit = n;
   a.num_pairs = n;
-  a.k_block_bytes = block_elems(pool) * k_elem_bytes(pool->dtype);
+  a.k_block_bytes = k_block_bytes(pool);
   a.v_block_bytes = block_elems(pool) * elem_bytes(pool->dtype);
   a.skip_equal = false;
   return from_hip(pa::launch_block_move(a, stream));
@@ -362,7 +404,7 @@ pa_status pa_scatter_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool
   a.dst_stride = 1;
   a.dst_limit = pool->num_blocks;
   a.num_pairs = n;
-  a.k_block_bytes = block_elems(pool) * k_elem_bytes(pool->dtype);
+  a.k_block_bytes = k_block_bytes(pool);
   a.v_block_bytes = block_elems(pool) * elem_bytes(pool->dtype);
   a.skip_equal = false;
   return from_hip(pa::launch_block_move(a, stream));

@@ -222,6 +222,63 @@ __global__ __launch_bounds__(256) void write_kv_k8_kernel(char* k_pool, char* v_
   }
 }
 
+// write_kv_k2: as write_kv, with each key element quantised to a 2-bit code
+// by its channel's step s and zero point z: u = (k - z) / s in float32 (IEEE
+// subtraction and division), code = rint(min(max(u, 0), 3)) (fminf/fmaxf drop a
+// NaN).  One thread per (token, KV head, key word): word (q, w) of a token holds
+// channels 32 j + 8 q + e for j = 2w + h, h = 0, 1, e = 0..7, the code of
+// channel 32 j + 8 q + 2 i + p at bit 2 (4 h + i) + 16 p -- two contiguous runs of
+// 8 channels of the new row.  A thread also copies the V elements of those 16
+// channels.
+template <class Tr, class E>
+__global__ __launch_bounds__(256) void write_kv_k2_kernel(char* k_pool, char* v_pool,
+                                                          const float* k_scale, const float* k_zero,
+                                                          const uint4* k_new, const uint4* v_new,
+                                                          const int64_t* slot_mapping,
+                                                          int num_tokens, int64_t num_slots, int bs,
+                                                          int num_kv_heads, int head_dim) {
+  const int cols = head_dim / 64;     // words per (group, token)
+  const int words = 4 * cols;         // words per token and KV head
+  const int per_token = num_kv_heads * words;
+  const int64_t total = static_cast<int64_t>(num_tokens) * per_token;
+  for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int tok = static_cast<int>(idx / per_token);
+    const int64_t slot = slot_mapping[tok];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int rem = static_cast<int>(idx % per_token);
+    const int g = rem / words;
+    const int q = (rem % words) / cols;
+    const int w = rem % cols;
+    const int64_t phys = slot / bs;
+    const int o = static_cast<int>(slot % bs);
+    const size_t tile = (static_cast<size_t>(phys) * num_kv_heads + g) * bs * head_dim;  // elements
+    const size_t row = (static_cast<size_t>(tok) * num_kv_heads + g) * head_dim;          // elements
+    uint32_t word = 0u;
+    E* vt = reinterpret_cast<E*>(v_pool) + tile;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c0 = 32 * (2 * w + h) + 8 * q;  // first of the 8 channels
+      float kf[8];
+      Tr::unpack(k_new[(row + c0) / 8], kf);
+      const float* sc = k_scale + static_cast<size_t>(g) * head_dim + c0;
+      const float* zp = k_zero + static_cast<size_t>(g) * head_dim + c0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float u = __fdiv_rn(kf[e] - zp[e], sc[e]);
+        u = __builtin_rintf(fminf(fmaxf(u, 0.f), 3.f));
+        word |= static_cast<uint32_t>(u) << (2 * (4 * h + e / 2) + 16 * (e % 2));
+      }
+      E ve[8];
+      __builtin_memcpy(ve, &v_new[(row + c0) / 8], 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[(c0 + e) * bs + o] = ve[e];
+    }
+    // word [q][o][w] of the tile: bs * head_dim / 16 words per tile
+    reinterpret_cast<uint32_t*>(k_pool)[tile / 16 + (static_cast<size_t>(q) * bs + o) * cols + w] = word;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // whole-block moves (copy-on-write copies, swap gather / scatter).  Pair p
 // moves block src(p) of the source K and V buffers to block dst(p) of the
@@ -324,6 +381,22 @@ hipError_t launch_write_kv_k8(void* k_pool, void* v_pool, const float* k_scale, 
                                    : write_kv_k8_kernel<BF16, uint16_t>;
   hipLaunchKernelGGL(kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
                      static_cast<char*>(k_pool), static_cast<char*>(v_pool), k_scale,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * block_size,
+                     block_size, num_kv_heads, head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv_k2(void* k_pool, void* v_pool, const float* k_scale, const float* k_zero,
+                              const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                              hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 16);
+  auto kernel = dtype == PA_K2_F16 ? write_kv_k2_kernel<F16, uint16_t>
+                                   : write_kv_k2_kernel<BF16, uint16_t>;
+  hipLaunchKernelGGL(kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream,
+                     static_cast<char*>(k_pool), static_cast<char*>(v_pool), k_scale, k_zero,
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
                      slot_mapping, num_tokens, static_cast<int64_t>(num_blocks) * block_size,
                      block_size, num_kv_heads, head_dim);

@@ -46,6 +46,8 @@
 //
 // Int8 keys (MmaK8) feed the same logits product with f16 operands: the codes
 // convert exactly and the per-channel scales ride on the query (see MmaK8).
+// 2-bit keys (MmaK2) do the same with one small load per tile; their zero
+// points become one logit offset per row (see MmaK2).
 //
 // Online softmax (§4.2 of the ialgorithm.me page: the normaliser is updated
 // while streaming, exactly): the running maximum m of each row is shared by
@@ -63,6 +65,8 @@
 // tokens past their own limit the same way (those V elements are real values
 // and meet weight 0).  A row that has seen no token keeps m = -inf and
 // contributes nothing.
+#include <type_traits>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -101,6 +105,10 @@ template <>
 struct NativeVec<uint2> {
   using type = u32x2;
 };
+template <>
+struct NativeVec<uint32_t> {
+  using type = uint32_t;
+};
 
 // Load with or without the non-temporal hint.  K and V are each read once per
 // call (shared-prefix blocks aside), so the streaming policy keeps them from
@@ -120,6 +128,8 @@ __device__ __forceinline__ T load16(const T* p) {
 // ---------------------------------------------------------------------------
 struct MmaBF16 {
   static constexpr int kKBytes = 2;  // bytes per K element
+  static constexpr int kKBits = 16;  // bits per K element
+  using KLoad = uint4;               // one lane's share of a K load
   static constexpr int kVBytes = 2;  // bytes per V (and q, out) element
   static constexpr int kQOps = 1;    // q operands per 16-byte K load
   using VLoad = uint2;  // 4 tokens of one V column
@@ -153,6 +163,8 @@ struct MmaBF16 {
 
 struct MmaF16 {
   static constexpr int kKBytes = 2;
+  static constexpr int kKBits = 16;
+  using KLoad = uint4;
   static constexpr int kVBytes = 2;
   static constexpr int kQOps = 1;
   using VLoad = uint2;
@@ -177,6 +189,8 @@ struct MmaF16 {
 
 struct MmaF32 {
   static constexpr int kKBytes = 4;
+  static constexpr int kKBits = 32;
+  using KLoad = uint4;
   static constexpr int kVBytes = 4;
   static constexpr int kQOps = 1;
   using VLoad = uint4;  // 4 tokens of one V column
@@ -222,6 +236,8 @@ struct MmaF32 {
 template <class VM>
 struct MmaK8 {
   static constexpr int kKBytes = 1;
+  static constexpr int kKBits = 8;
+  using KLoad = uint4;
   static constexpr int kVBytes = 2;
   static constexpr int kQOps = 2;
   using VLoad = typename VM::VLoad;
@@ -244,6 +260,54 @@ struct MmaK8 {
                                                0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes(k.z, k.w), __builtin_bit_cast(f16x8, q[1]), c,
                                                0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
+    return VM::pv(v, p, c);
+  }
+  static __device__ __forceinline__ POp pack(const float (&p)[4], float& sum) {
+    return VM::pack(p, sum);
+  }
+  static __device__ __forceinline__ void keep(VLoad& v, int n) { VM::keep(v, n); }
+};
+
+// 2-bit keys with float32 per-channel steps and zero points; values (and q,
+// out) of the 16-bit type of VM.  One load per tile: lane (r, q) reads the
+// D / 64 words of token r and channel group q (8 bytes at d 128, 4 at d 64),
+// which hold channels 32 j + 8 q + e (e = 0..7) for all D / 32 logit steps j:
+// step j is word j / 2, half j % 2, and ((word >> 2 (4 h + i)) & 0x30003) is
+// the pair of codes e = 2i, 2i + 1 in the low bits of two 16-bit halves.  Or-ing
+// in 0x6400 makes each half the f16 1024 + code; subtracting 1024 leaves the
+// code exactly.  The B operand is q' = q * step per channel (times a power of
+// two per row, as for int8 keys), and the zero points add the same
+// scale * sum_c q_c z_c to every logit of a row (kept in qb).
+template <class VM, int D>
+struct MmaK2 {
+  static constexpr int kKBytes = 0;  // sub-byte keys
+  static constexpr int kKBits = 2;
+  static constexpr int kVBytes = 2;
+  static constexpr int kQOps = D / 32;  // B operands per K load (one load per tile)
+  using KLoad = typename std::conditional<D == 128, uint2, uint32_t>::type;
+  using VLoad = typename VM::VLoad;
+  using POp = typename VM::POp;
+  static __device__ __forceinline__ uint32_t word(const KLoad& k, int i) {
+    if constexpr (D == 128) {
+      return i == 0 ? k.x : k.y;
+    } else {
+      return k;
+    }
+  }
+  static __device__ __forceinline__ f16x8 codes(uint32_t w, int h) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ((w >> (2 * (4 * h + i))) & 0x00030003u) | 0x64006400u;
+    return __builtin_bit_cast(f16x8, v) - static_cast<_Float16>(1024.0f);
+  }
+  static __device__ __forceinline__ f32x4 qk(const KLoad& k, const uint4* q, f32x4 c) {
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes(word(k, j / 2), j % 2),
+                                                 __builtin_bit_cast(f16x8, q[j]), c, 0, 0, 0);
     return c;
   }
   static __device__ __forceinline__ f32x4 pv(const VLoad& v, const POp& p, f32x4 c) {
@@ -336,7 +400,9 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // another, so their loads must not carry the streaming hint.
   constexpr bool kStreamK = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 2);
   constexpr bool kStreamV = !kShared && (PA_DECODE_NT == 1 || PA_DECODE_NT == 3);
-  constexpr int kKLoads = D * M::kKBytes / 64;  // 1 KiB K loads per tile (= 16-byte chunks / 4)
+  // K loads per tile: 1 KiB each (16-byte chunks / 4), or one smaller load
+  // covering a 2-bit tile
+  constexpr int kKLoads = D * M::kKBits / 512 > 0 ? D * M::kKBits / 512 : 1;
   constexpr int kQOps = kKLoads * M::kQOps;      // B operands of the logits per row
   constexpr int kColBlocks = D / 16;           // P.V output blocks of 16 columns
   constexpr int kPad = 4;                      // LDS row padding (floats)
@@ -345,6 +411,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // no merge through LDS; otherwise the waves share one partition's blocks.
   constexpr int kStride = kWavePart ? 1 : kStepWaves;  // logical-step stride of a wave
   using VLoad = typename M::VLoad;
+  using KLoad = typename M::KLoad;
 
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
@@ -381,7 +448,8 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // rows), its token limit, the scale of its logits and its online-softmax state.
   uint4 qop[kChunks][kQOps];
   int row_hi[kChunks];
-  float qs[kChunks];  // logits in log2 units: scale * log2(e) (and the K8 row factor)
+  float qs[kChunks];  // logits in log2 units: scale * log2(e) (and the quantised-key row factor)
+  float qb[kChunks];  // 2-bit keys: the zero points' logit offset of the row (log2 units)
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int rho = row0 + 16 * c + r;
@@ -392,13 +460,14 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
     const char* qrow = static_cast<const char*>(a.q) +
                        ((static_cast<size_t>(s) * T + i) * a.num_q_heads + hq) * D * M::kVBytes;
     qs[c] = a.scale * kLog2e;
-    if constexpr (M::kQOps == 1) {
+    qb[c] = 0.f;
+    if constexpr (M::kKBits >= 16) {
 #pragma unroll
       for (int j = 0; j < kKLoads; ++j) {
         const uint4 v = reinterpret_cast<const uint4*>(qrow)[4 * j + qg];
         qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
       }
-    } else {
+    } else if constexpr (M::kKBits == 8) {
       // int8 keys: load j brings channels 16 (4j + qg) .. + 15 of a token; the
       // matching q' = q * k_scale, scaled by 2^e so that the row's largest
       // |q'| lies in [2^13, 2^14) (full f16 precision whatever the scales),
@@ -441,6 +510,49 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
           qop[c][2 * j + hh] = live ? v : make_uint4(0u, 0u, 0u, 0u);
         }
       }
+    } else {
+      // 2-bit keys: operand j holds channels 32 j + 8 qg .. + 7 of q' = q * step,
+      // scaled as for int8 keys; the lane's share of sum_c q_c z_c joins the
+      // other three lanes of the row.
+      const float* ks = a.k_scale + static_cast<size_t>(g) * D;
+      const float* kz = a.k_zero + static_cast<size_t>(g) * D;
+      float qp[kQOps][8];
+      float mx = 0.f, zb = 0.f;
+#pragma unroll
+      for (int j = 0; j < kQOps; ++j) {
+        const int ch = 32 * j + 8 * qg;
+        float e[8];
+        Tr::unpack(reinterpret_cast<const uint4*>(qrow)[ch / 8], e);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float4 sc4 = reinterpret_cast<const float4*>(ks + ch)[t];
+          const float4 z4 = reinterpret_cast<const float4*>(kz + ch)[t];
+          qp[j][4 * t + 0] = e[4 * t + 0] * sc4.x;
+          qp[j][4 * t + 1] = e[4 * t + 1] * sc4.y;
+          qp[j][4 * t + 2] = e[4 * t + 2] * sc4.z;
+          qp[j][4 * t + 3] = e[4 * t + 3] * sc4.w;
+          zb += (e[4 * t + 0] * z4.x + e[4 * t + 1] * z4.y) + (e[4 * t + 2] * z4.z + e[4 * t + 3] * z4.w);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) mx = fmaxf(mx, fabsf(qp[j][t]));
+      }
+      mx = max_over_q(mx);  // the row's four lanes
+      zb = sum_over_q(zb);
+      int ex = 0;
+      if (mx > 0.f) {
+        (void)frexpf(mx, &ex);  // mx in [2^(ex-1), 2^ex)
+      }
+      const float up = ldexpf(1.f, 14 - ex);
+      qb[c] = zb * qs[c];
+      qs[c] *= ldexpf(1.f, ex - 14);
+#pragma unroll
+      for (int j = 0; j < kQOps; ++j) {
+        f16x8 h;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) h[t] = static_cast<_Float16>(qp[j][t] * up);
+        const uint4 v = __builtin_bit_cast(uint4, h);
+        qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
     row_hi[c] = live ? min(t_hi, L - T + 1 + i) : t_hi;
   }
@@ -481,19 +593,19 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // bytes per half wave); V tokens 4qg .. 4qg+3 are tokens 4 (qg % 2) .. of
   // block qg / 2.
   struct TilePtrs {
-    const uint4* kt;
+    const KLoad* kt;
     const VLoad* vt;
   };
   auto tile_ptrs = [&](Phys ph) {
     TilePtrs p;
     if constexpr (kBS == 16) {
       const size_t tile = pa_tile_offset(ph.a, g, a.num_kv_heads, D, 16);  // elements
-      p.kt = reinterpret_cast<const uint4*>(kbase + tile * M::kKBytes);
+      p.kt = reinterpret_cast<const KLoad*>(kbase + tile * M::kKBits / 8);
       p.vt = reinterpret_cast<const VLoad*>(vbase + tile * M::kVBytes);
     } else {
       const size_t ta = pa_tile_offset(ph.a, g, a.num_kv_heads, D, 8);
       const size_t tb = pa_tile_offset(ph.b, g, a.num_kv_heads, D, 8);
-      p.kt = reinterpret_cast<const uint4*>(kbase + (r < 8 ? ta : tb) * M::kKBytes);
+      p.kt = reinterpret_cast<const KLoad*>(kbase + (r < 8 ? ta : tb) * M::kKBits / 8);
       p.vt = reinterpret_cast<const VLoad*>(vbase + (qg < 2 ? ta : tb) * M::kVBytes);
     }
     return p;
@@ -504,7 +616,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   auto v_at = [&](const TilePtrs& p, int cb) {
     return kBS == 16 ? p.vt + (16 * cb + r) * 4 + qg : p.vt + (16 * cb + r) * 2 + (qg & 1);
   };
-  auto load = [&](Phys ph, uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
+  auto load = [&](Phys ph, KLoad (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
     const TilePtrs p = tile_ptrs(ph);
 #pragma unroll
     for (int j = 0; j < kKLoads; ++j) kr[j] = load16<kStreamK>(k_at(p, j));
@@ -512,7 +624,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
     for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = load16<kStreamV>(v_at(p, cb));
   };
 
-  auto consume = [&](int jb, const uint4 (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
+  auto consume = [&](int jb, const KLoad (&kr)[kKLoads], VLoad (&vr)[kColBlocks]) {
     const int tok0 = jb * kStep + 4 * qg;  // first token of this lane's four
     if ((jb + 1) * kStep > t_hi) {          // V rows past the partition (wave-uniform test)
       const int n = min(max(t_hi - tok0, 0), 4);
@@ -528,6 +640,10 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs[c];
+      if constexpr (M::kKBits == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] += qb[c];
+      }
       if (masked) {
         const int n = min(max(row_hi[c] - tok0, 0), 4);
 #pragma unroll
@@ -562,7 +678,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // the wait before each consume covers exactly the step consumed: a load that
   // may or may not have been issued would make the compiler wait for every
   // load in flight, the next steps' included.
-  uint4 kr[kDepth][kKLoads];
+  KLoad kr[kDepth][kKLoads];
   VLoad vr[kDepth][kColBlocks];
   const int first = blk_lo + (kWavePart ? 0 : sw);
   const int n = first < blk_hi ? (blk_hi - first + kStride - 1) / kStride : 0;
@@ -750,7 +866,10 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
 
 // Partitions of at least this many tokens get 8 wavefronts per workgroup (each
 // wave still streams a long run of blocks, and a ragged batch finishes more
-// evenly); shorter ones get 4.
+// evenly); shorter ones get 4.  2-bit keys always get 4: a step carries 4.5 KiB
+// instead of 8, and three 4-wave workgroups per compute unit keep more of them
+// in flight than one of 8 (measured on the 70B batch: 97.1 -> 92.9 us; ring
+// depths 3 and 4 changed nothing).
 constexpr int kWideTokens = 4096;
 
 // One wave per partition needs at least this many partitions per sequence and
@@ -787,7 +906,7 @@ hipError_t launch_cs(const DecodeArgs& a, int wgs, hipStream_t stream) {
   // Four chunks hold 64 rows of state per lane: only 4 waves per workgroup fit
   // them without spilling.
   if constexpr (kChunks < 4) {
-    if (a.partition_tokens >= kWideTokens) {
+    if (M::kKBits != 2 && a.partition_tokens >= kWideTokens) {
       hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kShared, kBS, false>), grid,
                          dim3(8 * 64), 0, stream, a);
       return hipGetLastError();
@@ -860,6 +979,11 @@ template <class M, class Tr>
 hipError_t launch_dim(const DecodeArgs& a, hipStream_t stream) {
   return a.head_dim == 64 ? launch_t<M, Tr, 64>(a, stream) : launch_t<M, Tr, 128>(a, stream);
 }
+template <class VM, class Tr>
+hipError_t launch_dim_k2(const DecodeArgs& a, hipStream_t stream) {
+  return a.head_dim == 64 ? launch_t<MmaK2<VM, 64>, Tr, 64>(a, stream)
+                          : launch_t<MmaK2<VM, 128>, Tr, 128>(a, stream);
+}
 
 }  // namespace
 
@@ -869,6 +993,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     case PA_F16: return launch_dim<MmaF16, F16>(a, stream);
     case PA_K8_F16: return launch_dim<MmaK8<MmaF16>, F16>(a, stream);
     case PA_K8_BF16: return launch_dim<MmaK8<MmaBF16>, BF16>(a, stream);
+    case PA_K2_F16: return launch_dim_k2<MmaF16, F16>(a, stream);
+    case PA_K2_BF16: return launch_dim_k2<MmaBF16, BF16>(a, stream);
     default: return launch_dim<MmaBF16, BF16>(a, stream);
   }
 }

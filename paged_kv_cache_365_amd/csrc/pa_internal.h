@@ -15,7 +15,8 @@ struct DecodeArgs {
   const void* q;
   const void* k_pool;
   const void* v_pool;
-  const float* k_scale;  // int8 keys: float32 [H_kv][d] channel scales; else null
+  const float* k_scale;  // quantised keys: float32 [H_kv][d] channel scales (steps); else null
+  const float* k_zero;   // 2-bit keys: float32 [H_kv][d] channel zero points; else null
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t max_blocks_per_seq;
@@ -84,6 +85,12 @@ hipError_t launch_write_kv_k8(void* k_pool, void* v_pool, const float* k_scale, 
                               const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
                               int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                               int32_t head_dim, int32_t dtype, hipStream_t stream);
+
+hipError_t launch_write_kv_k2(void* k_pool, void* v_pool, const float* k_scale, const float* k_zero,
+                              const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                              hipStream_t stream);
 
 hipError_t launch_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,

@@ -23,14 +23,15 @@ PA_ERR_WORKSPACE = -4
 PA_ERR_HIP = -5
 PA_ERR_NO_SPACE = -6
 
-PA_F32, PA_F16, PA_BF16, PA_K8_F16, PA_K8_BF16 = 0, 1, 2, 3, 4
+PA_F32, PA_F16, PA_BF16, PA_K8_F16, PA_K8_BF16, PA_K2_F16, PA_K2_BF16 = 0, 1, 2, 3, 4, 5, 6
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 NAME_TO_PA = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16}
 BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_init_pool", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
-           "pa_verify_decode", "pa_write_kv_k8", "pa_decode_k8", "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
+           "pa_verify_decode", "pa_write_kv_k8", "pa_decode_k8", "pa_write_kv_k2", "pa_decode_k2",
+           "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
            "pa_scatter_blocks", "pa_status_string")
 
 
@@ -79,6 +80,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_write_kv_k8.argtypes = [desc, vp, vp, vp, vp, vp, i64p, i32, vp]
     lib.pa_decode_k8.restype = ctypes.c_int
     lib.pa_decode_k8.argtypes = [desc, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
+                                 ctypes.c_float, i32, vp, sz, vp, vp]
+    lib.pa_write_kv_k2.restype = ctypes.c_int
+    lib.pa_write_kv_k2.argtypes = [desc, vp, vp, vp, vp, vp, vp, i64p, i32, vp]
+    lib.pa_decode_k2.restype = ctypes.c_int
+    lib.pa_decode_k2.argtypes = [desc, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                  ctypes.c_float, i32, vp, sz, vp, vp]
     lib.pa_reduce.restype = ctypes.c_int
     lib.pa_reduce.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
@@ -164,20 +170,30 @@ def _value_dtype(k_pool, v_pool):
 def pool_desc(k_pool: torch.Tensor, v_pool: torch.Tensor | None = None,
               chk: _Args | None = None) -> PoolDesc:
     """Descriptor of a K pool tensor shaped [num_blocks][H_kv][d / x][bs][x]
-    (with its V pool [num_blocks][H_kv][d][bs]).  An int8 K pool (quantised
-    keys) takes its value type from ``v_pool``."""
+    (with its V pool [num_blocks][H_kv][d][bs]).  Quantised key pools take
+    their value type from ``v_pool``: int8 [num_blocks][H_kv][d / 16][bs][16],
+    or 2-bit keys as int32 words [num_blocks][H_kv][4][bs][d / 64]."""
     chk = chk or _Args("pool_desc")
-    chk("k_pool", k_pool, (torch.int8,) + VALUE_TYPES, 5)
+    chk("k_pool", k_pool, (torch.int8, torch.int32) + VALUE_TYPES, 5)
     nb, hkv, nchunk, bs, x = k_pool.shape
+    if k_pool.dtype == torch.int32:
+        if nchunk != 4:
+            raise ValueError(f"{chk.fn}: a 2-bit key pool has shape [num_blocks][H_kv][4][bs]"
+                             f"[d / 64], got {tuple(k_pool.shape)}")
+        d = 64 * x
+    else:
+        d = nchunk * x
     if v_pool is not None:
-        want = VALUE_TYPES[1:] if k_pool.dtype == torch.int8 else k_pool.dtype
-        chk("v_pool", v_pool, want, 4, (nb, hkv, nchunk * x, bs))
-    if k_pool.dtype == torch.int8:
+        want = VALUE_TYPES[1:] if k_pool.dtype in (torch.int8, torch.int32) else k_pool.dtype
+        chk("v_pool", v_pool, want, 4, (nb, hkv, d, bs))
+    if k_pool.dtype in (torch.int8, torch.int32):
         vt = None if v_pool is None else v_pool.dtype
-        dt = {torch.float16: PA_K8_F16, torch.bfloat16: PA_K8_BF16}.get(vt, -1)
+        table = ({torch.float16: PA_K8_F16, torch.bfloat16: PA_K8_BF16} if k_pool.dtype == torch.int8
+                 else {torch.float16: PA_K2_F16, torch.bfloat16: PA_K2_BF16})
+        dt = table.get(vt, -1)
     else:
         dt = TORCH_TO_PA.get(k_pool.dtype, -1)
-    return PoolDesc(nb, bs, hkv, nchunk * x, dt)
+    return PoolDesc(nb, bs, hkv, d, dt)
 
 
 def pa_status_string(status: int) -> str:
@@ -283,6 +299,43 @@ def pa_decode_k8(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_con
         ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq, int(max_context_len),
         float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
+
+
+def pa_write_kv_k2(k_pool, v_pool, k_scale, k_zero, k_new, v_new, slot_mapping,
+                   stream=None) -> None:
+    """2-bit key pool (int32 words): k_new / v_new [T][H_kv][d] in the value type,
+    k_scale and k_zero float32 [H_kv][d]."""
+    chk = _Args("pa_write_kv_k2")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk("k_scale", k_scale, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
+    chk("k_zero", k_zero, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
+    chk("slot_mapping", slot_mapping, torch.int64, 1)
+    n = int(slot_mapping.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        chk(name, t, v_pool.dtype, 3, (n, desc.num_kv_heads, desc.head_dim))
+    chk.on_gpu()
+    _check("pa_write_kv_k2", load().pa_write_kv_k2(
+        ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(k_zero), _ptr(k_new),
+        _ptr(v_new), _ptr(slot_mapping), n, _stream(stream)))
+
+
+def pa_decode_k2(q, k_pool, v_pool, k_scale, k_zero, block_tables, context_lens,
+                 max_context_len: int, scale: float, partition_size: int = 0, workspace=None,
+                 out=None, stream=None) -> None:
+    """q and out: [B][T][H_q][d] in the value type (T = 1: decode)."""
+    chk = _Args("pa_decode_k2")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk("k_scale", k_scale, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
+    chk("k_zero", k_zero, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
+    _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, workspace, out, 4)
+    B, T, Hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    chk.on_gpu()
+    _check("pa_decode_k2", load().pa_decode_k2(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(k_zero),
+        _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq,
+        int(max_context_len), float(scale), int(partition_size), _ptr(workspace), ws_bytes,
+        _ptr(out), _stream(stream)))
 
 
 def pa_reduce(workspace, context_lens, num_seqs: int, num_q_heads: int, head_dim: int,
@@ -424,4 +477,26 @@ def k8_attention(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_con
     else:
         pa_decode_k8(q, k_pool, v_pool, k_scale, block_tables, context_lens, max_context_len, scale,
                      0, None, out, stream)
+    return out
+
+
+def k2_attention(q, k_pool, v_pool, k_scale, k_zero, block_tables, context_lens,
+                 max_context_len: int, scale: float, partition_size: int = 0, workspace=None,
+                 out=None, stream=None):
+    """out = pa_decode_k2 (+ pa_reduce over T * H_q rows when split).  q is
+    [B][T][H_q][d]; returns out of the same shape."""
+    if out is None:
+        out = torch.empty_like(q)
+    B, T, Hq, D = q.shape
+    if partition_size > 0:
+        if workspace is None:
+            n = pa_decode_workspace_bytes(B, T * Hq, D, max_context_len, partition_size)
+            workspace = torch.empty(n // 4, dtype=torch.float32, device=q.device)
+        pa_decode_k2(q, k_pool, v_pool, k_scale, k_zero, block_tables, context_lens,
+                     max_context_len, scale, partition_size, workspace, None, stream)
+        pa_reduce(workspace, context_lens, B, T * Hq, D, max_context_len, partition_size, out,
+                  stream)
+    else:
+        pa_decode_k2(q, k_pool, v_pool, k_scale, k_zero, block_tables, context_lens,
+                     max_context_len, scale, 0, None, out, stream)
     return out

@@ -181,7 +181,8 @@ class Workload:
         """KV + q + out + live block-table entries + context_lens (q and out hold
         ``query_tokens`` rows per sequence and head: 1 for decode, T for a verify
         call over a T-token draft).  With int8 keys (``key_bytes`` = 1) the
-        float32 channel scales are read too."""
+        float32 channel scales are read too, with 2-bit keys (``key_bytes`` =
+        0.25) the float32 channel steps and zero points."""
         e = ELEM_BYTES[self.dtype]
         qo = 2 * query_tokens * self.num_seqs * self.num_q_heads * self.head_dim * e
         bs = self.block_size
@@ -190,7 +191,7 @@ class Workload:
             kv = self.kv_bytes_unique()
         else:
             kv = self.kv_bytes_logical(key_bytes)
-        scales = 4 * self.num_kv_heads * self.head_dim if key_bytes == 1 else 0
+        scales = {1: 4, 0.25: 8}.get(key_bytes, 0) * self.num_kv_heads * self.head_dim
         return kv + qo + 4 * live_entries + 4 * self.num_seqs + scales
 
 
@@ -227,6 +228,31 @@ def k8_inputs(w: "Workload", seed: int, outlier_columns: int = 0, outlier_gain: 
         if L and o:
             codes[w.block_tables[s, L // bs], :, :, o:, :] = K8_POISON
     return codes, k_scale
+
+
+K2_BASE_STEP = 1.4         # 2-bit codes 0..3 at -2.1, -0.7, 0.7, 2.1: a coarse N(0,1) key
+K2_BASE_ZERO = -2.1
+
+
+def k2_inputs(w: "Workload", seed: int, outlier_columns: int = 0, outlier_gain: float = 10.0):
+    """A 2-bit key cache for ``w``'s pool, tables and shapes (``w``'s V pool, q
+    and tables are used with it): key words [NB][H_kv][4][bs][d/64] of uniform
+    random bits (every 2-bit code equally likely, free blocks and tail slots
+    included: every pattern is a code, so unread slots are shown unread by the
+    NaN V pool), float32 channel steps [H_kv][d] of 1.4 and zero points of
+    -2.1, both times ``outlier_gain`` on ``outlier_columns`` random (KV head,
+    channel) columns -- the per-channel key outliers.  Returns (k2_pool uint32,
+    k_scale float32, k_zero float32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    NB, Hkv, d, bs = w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size
+    words = rng.integers(0, 2 ** 32, size=(NB, Hkv, 4, bs, d // 64), dtype=np.uint32)
+    k_scale = np.full((Hkv, d), K2_BASE_STEP, dtype=np.float32)
+    k_zero = np.full((Hkv, d), K2_BASE_ZERO, dtype=np.float32)
+    if outlier_columns:
+        cols = rng.choice(Hkv * d, size=outlier_columns, replace=False)
+        k_scale.reshape(-1)[cols] *= np.float32(outlier_gain)
+        k_zero.reshape(-1)[cols] *= np.float32(outlier_gain)
+    return words, k_scale, k_zero
 
 
 def _scale_for(head_dim: int) -> float:

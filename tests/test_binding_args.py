@@ -75,6 +75,16 @@ def test_append_and_verify_arguments():
     k8 = torch.zeros((4, 2, 8, 16, 16), dtype=torch.int8)
     _raises("pa_decode_k8: k_scale has shape", pa.pa_decode_k8, q4, k8, vp,
             torch.zeros((2, 64)), tables, lens, 40, 0.1)
+    k2 = torch.zeros((4, 2, 4, 16, 2), dtype=torch.int32)
+    ones = torch.ones((2, 128))
+    _raises("pa_decode_k2: k_zero has shape", pa.pa_decode_k2, q4, k2, vp, ones,
+            torch.zeros((2, 64)), tables, lens, 40, 0.1)
+    _raises("pa_decode_k2: k_zero is torch.float64", pa.pa_decode_k2, q4, k2, vp, ones,
+            ones.double(), tables, lens, 40, 0.1)
+    _raises("a 2-bit key pool has shape", pa.pa_decode_k2, q4,
+            torch.zeros((4, 2, 8, 16, 2), dtype=torch.int32), vp, ones, ones, tables, lens, 40, 0.1)
+    _raises("pa_write_kv_k2: v_new has shape", pa.pa_write_kv_k2, k2, vp, ones, ones, kn,
+            kn[:2].contiguous(), slots)
 
 
 def test_reduce_and_block_move_arguments():

@@ -178,3 +178,34 @@ def test_k8_calls_reject_bad_arguments(lib):
     # pa_reduce writes a plain 16-bit output
     assert lib.pa_reduce(FAKE, FAKE, 2, 4, 64, 40, 16, pa.PA_K8_BF16, FAKE, None) == pa.PA_ERR_UNSUPPORTED
     assert pa.pa_status_string(pa.PA_OK) == "PA_OK"
+
+
+def test_k2_calls_reject_bad_arguments(lib):
+    k2 = _desc(dtype=pa.PA_K2_BF16)
+    k8 = _desc(dtype=pa.PA_K8_BF16)
+    plain = _desc(dtype=pa.PA_BF16)
+    w2 = lib.pa_write_kv_k2
+    assert w2(ctypes.byref(k2), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == pa.PA_OK
+    assert w2(ctypes.byref(plain), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    assert w2(ctypes.byref(k8), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    assert w2(ctypes.byref(k2), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_INVALID_ARG
+    assert w2(ctypes.byref(k2), FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_MISALIGNED
+    # the plain and int8 calls refuse a 2-bit key pool
+    assert lib.pa_write_kv(ctypes.byref(k2), FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_write_kv_k8(ctypes.byref(k2), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, None) == pa.PA_ERR_UNSUPPORTED
+    assert _decode(lib, desc=k2) == pa.PA_ERR_UNSUPPORTED
+    d2 = lib.pa_decode_k2
+
+    def call(desc=k2, ks=FAKE, kz=FAKE, T=1, q=FAKE):
+        return d2(ctypes.byref(desc), q, FAKE, FAKE, ks, kz, FAKE, 4, FAKE, 2, T, 4, 40, 0.125, 0,
+                  None, 0, FAKE, None)
+    assert call(ks=None) == pa.PA_ERR_INVALID_ARG
+    assert call(kz=None) == pa.PA_ERR_INVALID_ARG
+    assert call(desc=plain) == pa.PA_ERR_UNSUPPORTED
+    assert call(desc=k8) == pa.PA_ERR_UNSUPPORTED
+    assert call(kz=FAKE + 4) == pa.PA_ERR_MISALIGNED      # zero points are read 16 bytes at a time
+    assert call(T=0) == pa.PA_ERR_INVALID_ARG
+    d8 = lib.pa_decode_k8
+    assert d8(ctypes.byref(k2), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 1, 4, 40, 0.125, 0,
+              None, 0, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_reduce(FAKE, FAKE, 2, 4, 64, 40, 16, pa.PA_K2_BF16, FAKE, None) == pa.PA_ERR_UNSUPPORTED
