@@ -282,15 +282,18 @@ def main() -> int:
     log(f"timed {args.steps} steps in {wall * 1e3:.2f} ms "
         f"(device {device_ms_per_step * 1e3:.2f} us/step)")
 
+    # Second pass of K steps with an event pair around every launch: the
+    # distribution of single-launch durations (p10 / median / p90), and for a
+    # split step, which is two kernels, the decode launch's own mean.
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    launch_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    launch_pct = {f"p{q}": round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
     if P:
-        # A split step is two kernels: time the decode launches on their own,
-        # one event pair around each, in a second pass of K steps.
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                  for _ in range(args.steps)]
-        for k in range(args.steps):
-            step(events[k])
-        torch.cuda.synchronize()
-        decode_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+        decode_ms = float(np.mean(launch_ms))
         reduce_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
         duration_source = "HIP events around each pa_decode launch (second pass of K steps)"
     else:
@@ -334,6 +337,7 @@ def main() -> int:
         "device_us_per_step": round(device_ms_per_step * 1e3, 2),
         "decode_us": round(decode_ms * 1e3, 2),
         "reduce_us": round(reduce_ms * 1e3, 2),
+        "decode_launch_us": launch_pct,
         "roofline": {
             "kernel": ("pa_decode_k8" if k8 else "pa_decode_k2" if k2 else
                        "pa_verify_decode" if args.verify else "pa_decode"),

@@ -4,8 +4,9 @@ ties, clamping, the zero-step channel, 16- and 8-token blocks), decode and
 verify against the fp64 attention over the dequantised keys z + s * code
 (tolerance 2e-2, the 16-bit value type's), split partials including the zero
 points' share of the log-sum-exp, block moves on pools whose K blocks are 1/8
-of the V blocks, and the 70B-style batch with per-channel key outliers at full
-size.
+of the V blocks, and at full size the 70B-style batch with per-channel key
+outliers, the long-context workload at its 512-token partitions and the
+7B-style ragged MHA batch.
 """
 import numpy as np
 import pytest
@@ -207,3 +208,25 @@ def test_k2_70b_gqa_4k_sampled():
         want = qk.paged_decode_k2(q[s:s + 1], words, w.v_pool, w.block_tables[s:s + 1],
                                   w.context_lens[s:s + 1], w.scale, step, zero, w.dtype)[0, 0]
         assert np.abs(got[s] - want).max() <= TOL, s
+
+
+@pytest.mark.parametrize("cfg,P,seqs", [(4, 512, (0, 3)), (1, 0, (0, 13, 31))])
+def test_k2_full_size_workloads(cfg, P, seqs):
+    """2-bit keys over the long-context workload (4 x 32768 tokens, 64/8 heads)
+    split into its own 512-token partitions and merged by pa_reduce, and over
+    the 7B-style ragged MHA batch (32 x U[512, 4096] tokens, 32/32 heads,
+    f16) unsplit; whole sequences against the oracle."""
+    w = wl.make_config(cfg)
+    words, step, zero = wl.k2_inputs(w, 2060 + cfg)
+    dw = upload(w, DEV)
+    q = w.q[:, None]
+    out = pa.k2_attention(to_torch(q, w.dtype, DEV), k2_tensor(words), dw.v_pool, f32_tensor(step),
+                          f32_tensor(zero), dw.block_tables, dw.context_lens, w.max_context_len,
+                          w.scale, partition_size=P)
+    torch.cuda.synchronize()
+    got = widen_f32(out)[:, 0]
+    assert np.isfinite(got).all()
+    for s in seqs:
+        want = qk.paged_decode_k2(q[s:s + 1], words, w.v_pool, w.block_tables[s:s + 1],
+                                  w.context_lens[s:s + 1], w.scale, step, zero, w.dtype)[0, 0]
+        assert np.abs(got[s] - want).max() <= TOL, (w.name, s)
