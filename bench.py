@@ -160,6 +160,10 @@ def main() -> int:
                     help="k8: int8 keys with per-channel scales (pa_decode_k8); k2: 2-bit keys "
                          "with per-channel steps and zero points (pa_decode_k2); values in the "
                          "workload's 16-bit type")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="time pa_decode_shared_prefix (+ pa_reduce): the prefix every table "
+                         "starts with computed once per KV head for the whole batch "
+                         "(shared-prefix workload; the partition size must divide the prefix)")
     ap.add_argument("--verify", type=int, default=0, metavar="T",
                     help="time the speculative-decoding verify call over a T-token draft "
                          "(pa_verify_decode) instead of single-token decode")
@@ -194,6 +198,12 @@ def main() -> int:
         w = dataclasses.replace(w, q=w.q[order], block_tables=w.block_tables[order],
                                 context_lens=w.context_lens[order])
     P = tuning.partition_for(w, own=not args.tuned) if args.partition is None else args.partition
+    prefix_tokens = w.prefix_blocks * w.block_size
+    if args.shared_prefix and (not prefix_tokens or P <= 0 or prefix_tokens % P or args.verify or
+                               args.kv != "native"):
+        print("--shared-prefix needs a workload with a shared prefix, a partition size that "
+              "divides it, one query token and the native KV type", file=sys.stderr)
+        return 2
     d = upload(w, "cuda")
     T = max(args.verify, 1)
     B, Hq, D = d.q.shape
@@ -247,6 +257,9 @@ def main() -> int:
         elif k8:
             pa.pa_decode_k8(qv, k8_pool, d.v_pool, k8_scale, d.block_tables, d.context_lens,
                             d.max_context_len, d.scale, P, ws, None if P else out, stream)
+        elif args.shared_prefix:
+            pa.pa_decode_shared_prefix(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                                       d.max_context_len, d.scale, prefix_tokens, P, ws, stream)
         elif args.verify:
             pa.pa_verify_decode(qv, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
                                 d.max_context_len, d.scale, P, ws, None if P else out, stream)
@@ -308,7 +321,7 @@ def main() -> int:
     kbytes = decode_kernel_bytes(w, P, T, key_bytes)
     achieved = kbytes / (decode_ms * 1e-3) / 1e9
     workload = (w.name + ("-k8" if k8 else "") + ("-k2" if k2 else "") +
-                (f"-verify{T}" if args.verify else ""))
+                (f"-verify{T}" if args.verify else "") + ("-sp" if args.shared_prefix else ""))
     traffic = stored_traffic(workload, P)
 
     rec = {
@@ -340,7 +353,8 @@ def main() -> int:
         "decode_launch_us": launch_pct,
         "roofline": {
             "kernel": ("pa_decode_k8" if k8 else "pa_decode_k2" if k2 else
-                       "pa_verify_decode" if args.verify else "pa_decode"),
+                       "pa_verify_decode" if args.verify else
+                       "pa_decode_shared_prefix" if args.shared_prefix else "pa_decode"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -351,6 +365,10 @@ def main() -> int:
             "duration_source": duration_source,
         },
     }
+    if w.prefix_blocks:
+        # shared blocks counted once: the bytes a step must take from memory
+        rec["unique_bytes_per_step"] = w.algorithmic_bytes(unique=True, query_tokens=T)
+        rec["unique_gbps"] = round(rec["unique_bytes_per_step"] / (ms_per_step * 1e-3) / 1e9, 2)
     if copy_gbps is not None:
         rec["device_copy_gbps"] = round(copy_gbps, 1)
     del d, out, ws

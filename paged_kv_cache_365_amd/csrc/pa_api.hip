@@ -134,7 +134,7 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
                         const int32_t* context_lens, int32_t num_seqs, int32_t num_query_tokens,
                         int32_t num_q_heads, int32_t max_context_len, float scale,
                         int32_t partition_size, void* workspace, size_t workspace_bytes, void* out,
-                        hipStream_t stream) {
+                        hipStream_t stream, int32_t prefix_tokens = 0) {
   pa_status st = check_pool(pool);
   if (st != PA_OK) return st;
   if (!q || !k_pool || !v_pool || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
@@ -189,6 +189,7 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
                          pa::kStep;
     a.partition_tokens = static_cast<int32_t>(span < pa::kStep ? pa::kStep : span);
     a.num_parts = 1;
+    a.part_stride = 1;
     a.write_partials = false;
     a.out = out;
   } else {
@@ -198,10 +199,19 @@ pa_status decode_common(const pa_pool_desc* pool, const void* q, const void* k_p
     if (!aligned(workspace, 16)) return PA_ERR_MISALIGNED;
     a.partition_tokens = partition_size;
     a.num_parts = num_parts_for(max_context_len, partition_size);
+    a.part_stride = a.num_parts;
     a.write_partials = true;
     const size_t nrows = static_cast<size_t>(num_seqs) * row_heads * a.num_parts;
     a.o_part = static_cast<float*>(workspace);
     a.lse_part = a.o_part + nrows * pool->head_dim;
+  }
+  if (prefix_tokens > 0) {
+    // the shared prefix is the first prefix_tokens / partition_size partitions
+    a.shared_parts = prefix_tokens / partition_size;
+    a.shared_tokens = prefix_tokens;
+    a.part_offset = a.shared_parts;
+    a.num_parts = a.part_stride - a.shared_parts;  // private partitions in the grid
+    return from_hip(pa::launch_decode_shared_prefix(a, stream));
   }
   return from_hip(pa::launch_decode(a, stream));
 }
@@ -245,6 +255,22 @@ pa_status pa_decode_k8(const pa_pool_desc* pool, const void* q, const void* k_po
   return decode_common(pool, q, k_pool, v_pool, k_scale, nullptr, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, num_query_tokens, num_q_heads, max_context_len,
                        scale, partition_size, workspace, workspace_bytes, out, stream);
+}
+
+pa_status pa_decode_shared_prefix(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                                  const void* v_pool, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                  float scale, int32_t prefix_tokens, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (pool && is_quantized(pool->dtype)) return PA_ERR_UNSUPPORTED;
+  if (partition_size <= 0 || prefix_tokens <= 0 || prefix_tokens % partition_size != 0 ||
+      prefix_tokens > max_context_len)
+    return PA_ERR_INVALID_ARG;
+  // always split: partials into the workspace, merged by pa_reduce
+  return decode_common(pool, q, k_pool, v_pool, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, 1, num_q_heads, max_context_len, scale,
+                       partition_size, workspace, workspace_bytes, nullptr, stream, prefix_tokens);
 }
 
 pa_status pa_write_kv_k8(const pa_pool_desc* pool, void* k_pool, void* v_pool, const float* k_scale,

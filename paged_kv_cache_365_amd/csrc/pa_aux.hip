@@ -8,37 +8,43 @@ namespace pa {
 namespace {
 
 // ---------------------------------------------------------------------------
-// pa_reduce: one wavefront per (row, 32-column slice), four per workgroup.  The
+// pa_reduce: one wavefront per (row, column slice), four per workgroup.  The
 // partition results are re-weighted by their share of the softmax mass: with
 // M = max lse_p, weight_p = exp(lse_p - M) / sum_q exp(lse_q - M).  This is the
 // same streaming-normaliser identity that makes the online softmax exact (§4.2
 // of the ialgorithm.me page).
-//   lane l = 8 g + c: float4 column c of the slice, partitions g, g + 8, ...;
+//   lane l = C g + c (C = 64 / kGroups float4 columns, a slice of 4 C columns):
+//   float4 column c of the slice, partitions g, g + kGroups, ...;
 //   1. the first kPre partials of the lane and their lse are loaded before
 //      anything else (they need no weight), the maximum M is a lane-strided
 //      scan of the live lse values and a butterfly over the wavefront;
 //   2. each lane weights and sums its partitions and their weights;
-//   3. a butterfly over the eight partition groups (lane bits 3..5) adds the
-//      group sums; lanes 0..7 normalise and store.
+//   3. a butterfly over the partition groups adds the group sums; the lanes of
+//      group 0 normalise and store.
+// kGroups = 8 (32-column slices) for many partitions; with at most 4 or 2
+// partitions per row, 4 or 2 groups and 64- or 128-column slices, so a row
+// takes fewer wavefronts and fewer lanes idle (shared-prefix batch, 2
+// partitions per row: 16384 -> 4096 wavefronts).
 // No LDS and no barrier.  Every sum has a fixed order and the butterfly gives
 // every lane the same bits, so the result is reproducible run to run.
 // ---------------------------------------------------------------------------
 constexpr int kReduceWaves = 4;    // wavefronts per workgroup
-constexpr int kSliceCols = 32;     // output columns per wavefront
-constexpr int kPartGroups = 8;     // partition groups per wavefront (x 8 float4 columns = 64 lanes)
 
-template <class Tr, int D>
+template <class Tr, int D, int kGroups>
 __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a) {
+  constexpr int kCols = 64 / kGroups;      // float4 columns per slice
+  constexpr int kSliceCols = 4 * kCols;    // output columns per wavefront
+  static_assert(kSliceCols <= D, "a slice lies inside one row");
   constexpr int kSlices = D / kSliceCols;
-  constexpr int kPre = 8;  // partials per lane loaded up front
+  constexpr int kPre = kGroups == 8 ? 8 : 1;  // partials per lane loaded up front
   const int lane = threadIdx.x & 63;
   const int64_t unit = static_cast<int64_t>(blockIdx.x) * kReduceWaves + (threadIdx.x >> 6);
   if (unit >= static_cast<int64_t>(a.num_seqs) * a.num_q_heads * kSlices) return;
   const int64_t row = unit / kSlices;
   const int slice = static_cast<int>(unit % kSlices);
   const int s = static_cast<int>(row / a.num_q_heads);
-  const int c4 = lane % (kSliceCols / 4);
-  const int grp = lane / (kSliceCols / 4);
+  const int c4 = lane % kCols;
+  const int grp = lane / kCols;
   const int col = slice * kSliceCols + 4 * c4;
   const float* lse = a.lse_part + row * a.num_parts;
   const float* op = a.o_part + row * a.num_parts * D + col;
@@ -47,7 +53,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a)
   float lpre[kPre];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) {
-    const int p = grp + i * kPartGroups;
+    const int p = grp + i * kGroups;
     if (p < a.num_parts) {
       pre[i] = *reinterpret_cast<const float4*>(op + static_cast<size_t>(p) * D);
       lpre[i] = lse[p];
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a)
   if (M != -INFINITY) {  // wavefront-uniform: an empty context stores a zero row
 #pragma unroll
     for (int i = 0; i < kPre; ++i) {
-      if (grp + i * kPartGroups < nv) {
+      if (grp + i * kGroups < nv) {
         const float w = __expf(lpre[i] - M);
         acc.x = fmaf(w, pre[i].x, acc.x);
         acc.y = fmaf(w, pre[i].y, acc.y);
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a)
       }
     }
 #pragma unroll 4
-    for (int p = grp + kPre * kPartGroups; p < nv; p += kPartGroups) {
+    for (int p = grp + kPre * kGroups; p < nv; p += kGroups) {
       const float w = __expf(lse[p] - M);
       const float4 v = *reinterpret_cast<const float4*>(op + static_cast<size_t>(p) * D);
       acc.x = fmaf(w, v.x, acc.x);
@@ -88,12 +94,11 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a)
       acc.w = fmaf(w, v.w, acc.w);
       wsum += w;
     }
-    constexpr int kGroupLanes = kSliceCols / 4;  // lanes of one partition group
-    acc.x = across_groups_sum<kGroupLanes>(acc.x);
-    acc.y = across_groups_sum<kGroupLanes>(acc.y);
-    acc.z = across_groups_sum<kGroupLanes>(acc.z);
-    acc.w = across_groups_sum<kGroupLanes>(acc.w);
-    wsum = across_groups_sum<kGroupLanes>(wsum);
+    acc.x = across_groups_sum<kCols>(acc.x);
+    acc.y = across_groups_sum<kCols>(acc.y);
+    acc.z = across_groups_sum<kCols>(acc.z);
+    acc.w = across_groups_sum<kCols>(acc.w);
+    wsum = across_groups_sum<kCols>(wsum);
     const float inv = 1.f / wsum;
     acc.x *= inv;
     acc.y *= inv;
@@ -109,16 +114,23 @@ __global__ __launch_bounds__(64 * kReduceWaves) void reduce_kernel(ReduceArgs a)
   }
 }
 
+template <class Tr, int D, int kGroups>
+hipError_t launch_reduce_g(const ReduceArgs& a, hipStream_t stream) {
+  constexpr int kSlices = D / (256 / kGroups);
+  const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_q_heads * kSlices;
+  const dim3 grid(static_cast<uint32_t>((units + kReduceWaves - 1) / kReduceWaves));
+  hipLaunchKernelGGL((reduce_kernel<Tr, D, kGroups>), grid, dim3(64 * kReduceWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <class Tr>
 hipError_t launch_reduce_t(const ReduceArgs& a, hipStream_t stream) {
-  const int slices = a.head_dim / kSliceCols;
-  const int64_t units = static_cast<int64_t>(a.num_seqs) * a.num_q_heads * slices;
-  const dim3 grid(static_cast<uint32_t>((units + kReduceWaves - 1) / kReduceWaves));
   if (a.head_dim == 64)
-    hipLaunchKernelGGL((reduce_kernel<Tr, 64>), grid, dim3(64 * kReduceWaves), 0, stream, a);
-  else
-    hipLaunchKernelGGL((reduce_kernel<Tr, 128>), grid, dim3(64 * kReduceWaves), 0, stream, a);
-  return hipGetLastError();
+    return a.num_parts <= 4 ? launch_reduce_g<Tr, 64, 4>(a, stream)
+                            : launch_reduce_g<Tr, 64, 8>(a, stream);
+  if (a.num_parts <= 2) return launch_reduce_g<Tr, 128, 2>(a, stream);
+  return a.num_parts <= 4 ? launch_reduce_g<Tr, 128, 4>(a, stream)
+                          : launch_reduce_g<Tr, 128, 8>(a, stream);
 }
 
 // ---------------------------------------------------------------------------

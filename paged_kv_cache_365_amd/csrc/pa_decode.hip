@@ -386,13 +386,14 @@ constexpr int min_waves_per_simd() {
 }
 
 template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared, int kBS,
-          bool kWavePart, bool kLds = false>
+          bool kWavePart, bool kLds = false, bool kPrefix = false>
 __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>())) void decode_kernel(
     DecodeArgs a) {
   // kLds: four waves hold the four 16-row chunks of 64 rows and share each
   // step's tile through an LDS ring (see below); otherwise every wave holds all
   // kChunks chunks of the workgroup's rows and the waves split the steps.
   static_assert(!kLds || (kWaves == 4 && kChunks == 1 && !kWavePart), "LDS ring: 4 x 16 rows");
+  static_assert(!kPrefix || !kLds, "shared prefix: register path");
   constexpr int kRowWaves = kLds ? 4 : 1;            // waves that split the rows
   constexpr int kStepWaves = kWaves / kRowWaves;     // waves that split the steps
   constexpr int kWgRows = 16 * kChunks * kRowWaves;  // rows of one workgroup
@@ -419,29 +420,43 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   const int wave = wave_id();
   const int rw = wave % kRowWaves;  // this wave's chunk of the workgroup's rows
   const int sw = wave / kRowWaves;  // this wave's share of the steps
-  const int T = a.num_query_tokens;
+  // kPrefix: the first a.shared_units workgroups take the prefix role -- the
+  // partitions [0, a.shared_parts) of the prefix every table starts with,
+  // for the rows of all sequences at once (as if the batch were one sequence
+  // with a num_seqs-token query, read through table row 0, without a causal
+  // limit); the others compute each sequence's partitions from a.part_offset.
+  const bool prefix_role = kPrefix && static_cast<int>(blockIdx.x) < a.shared_units;
+  const int T = prefix_role ? a.num_seqs : a.num_query_tokens;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int rows = T * group;  // (query token, query head) rows that read KV head g
   const int wgs = (rows + kWgRows - 1) / kWgRows;
-  const int part_units = kWavePart ? (a.num_parts + kWaves - 1) / kWaves : a.num_parts;
-  const Unit u = unit_of(blockIdx.x, gridDim.x, wgs, part_units, a.num_kv_heads);
-  const int part = kWavePart ? u.part * kWaves + wave : u.part;
+  const int grid_parts = prefix_role ? a.shared_parts : a.num_parts;
+  const int part_units = kWavePart ? (grid_parts + kWaves - 1) / kWaves : grid_parts;
+  const int first_unit = kPrefix && !prefix_role ? a.shared_units : 0;
+  const int role_units = kPrefix ? (prefix_role ? a.shared_units : gridDim.x - a.shared_units)
+                                 : gridDim.x;
+  const Unit u = unit_of(blockIdx.x - first_unit, role_units, wgs, part_units, a.num_kv_heads);
+  const int gpart = kWavePart ? u.part * kWaves + wave : u.part;  // partition within the grid
+  const int part = gpart + (prefix_role ? 0 : a.part_offset);
   const int g = u.kv_head;
   const int row0 = u.sibling * kWgRows + rw * (16 * kChunks);
   const int s = u.seq;
-  if (kWavePart && part >= a.num_parts) return;  // a wave past the last partition (no barriers)
+  if (kWavePart && gpart >= grid_parts) return;  // a wave past the last partition (no barriers)
 
-  const int L = pa_clamp_len(a.context_lens[s], a.max_context_len);
+  const int L = prefix_role ? a.shared_tokens : pa_clamp_len(a.context_lens[s], a.max_context_len);
+  // causal reference: query token i sees the tokens [0, Lc - T + 1 + i); the
+  // prefix role's rows see all L tokens
+  const int Lc = prefix_role ? L + T - 1 : L;
   const int t_lo = part * a.partition_tokens;
   const int t_hi = min(L, t_lo + a.partition_tokens);
   // 16-token steps of the partition (a step is one 16-token block or two
   // 8-token blocks)
   const int blk_lo = t_lo / kStep;
   const int blk_hi = t_hi > t_lo ? (t_hi + kStep - 1) / kStep : blk_lo;
-  // Query token i sees the tokens [0, L - T + 1 + i) (the draft is causal; one
+  // Query token i sees the tokens [0, Lc - T + 1 + i) (the draft is causal; one
   // query token sees the whole context).  Blocks that end past the smallest
   // limit of this wave's rows are masked row by row.
-  const int t_hi_min = min(t_hi, L - T + 1 + row0 / group);
+  const int t_hi_min = min(t_hi, Lc - T + 1 + row0 / group);
 
   // Per chunk c, lane l holds row row0 + 16 c + r: the B operands of its logits
   // (for 16-bit keys chunk 4j + qg of that row's query vector; zero for padding
@@ -554,7 +569,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
         qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    row_hi[c] = live ? min(t_hi, L - T + 1 + i) : t_hi;
+    row_hi[c] = live ? min(t_hi, Lc - T + 1 + i) : t_hi;
   }
 
   float m[kChunks];     // running maximum (log2 units) of row r, shared by its 4 lanes
@@ -799,12 +814,12 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
       const size_t row = (static_cast<size_t>(s) * T + rho / group) * a.num_q_heads +
                          g * group + rho % group;
       if (a.write_partials) {
-        float* op = a.o_part + (row * a.num_parts + part) * D + 4 * qg;
+        float* op = a.o_part + (row * a.part_stride + part) * D + 4 * qg;
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb)
           *reinterpret_cast<f32x4*>(op + 16 * cb) = acc[c][cb] * inv;
         if (qg == 0)
-          a.lse_part[row * a.num_parts + part] = seen ? (m[c] + __log2f(ls)) * kLn2 : -INFINITY;
+          a.lse_part[row * a.part_stride + part] = seen ? (m[c] + __log2f(ls)) * kLn2 : -INFINITY;
       } else {
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb)
@@ -855,8 +870,8 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
       const size_t row = (static_cast<size_t>(s) * T + rho / group) * a.num_q_heads +
                          g * group + rho % group;
       if (a.write_partials) {
-        a.o_part[(row * a.num_parts + part) * D + col] = o;
-        if (col == 0) a.lse_part[row * a.num_parts + part] = lse;
+        a.o_part[(row * a.part_stride + part) * D + col] = o;
+        if (col == 0) a.lse_part[row * a.part_stride + part] = lse;
       } else {
         Tr::store(a.out, row * D + col, o);
       }
@@ -985,6 +1000,62 @@ hipError_t launch_dim_k2(const DecodeArgs& a, hipStream_t stream) {
                           : launch_t<MmaK2<VM, 128>, Tr, 128>(a, stream);
 }
 
+// Shared-prefix split launch: one grid, prefix-role workgroups first (the
+// prefix partitions of every KV head, for all sequences' rows: siblings of
+// 16 * kChunks rows placed on one XCD, so each prefix tile leaves HBM once and
+// the siblings read it from that XCD's L2), then one workgroup per (sequence,
+// KV head, private partition), spread over all XCDs.  Both roles run the same
+// register-path kernel (the prefix role's rows are only wider in number).
+// Measured on the shared-prefix batch (128 sequences, 1024 shared + U[16,
+// 1024] private tokens, 32/8 heads; decode kernel, us): loads without the
+// streaming hint, so that siblings find the prefix in L2: 61.9 -> 57.2 at
+// 1024-token partitions, 69.9 -> 62.1 at 512; one wave per partition up to
+// 512 tokens (private units are short): 62.1 -> 57.2 at 512, 73.2 -> 62.2 at
+// 256.  pa_decode on the same batch: 70.4 (1024-token partitions).
+constexpr int kPrefixWavePartTokens = 512;
+template <class M, class Tr, int D, int kChunks, int kBS>
+hipError_t launch_prefix_c(DecodeArgs a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int64_t prefix_wgs = (static_cast<int64_t>(a.num_seqs) * group + 16 * kChunks - 1) / (16 * kChunks);
+  const int64_t private_wgs = (group + 16 * kChunks - 1) / (16 * kChunks);
+  constexpr bool kPlain = true;  // kShared: loads without the streaming hint
+  if (a.partition_tokens <= kPrefixWavePartTokens) {
+    // one wave per partition, four partitions per workgroup, in both roles
+    const int64_t shared = a.num_kv_heads * prefix_wgs * ((a.shared_parts + 3) / 4);
+    const int64_t total = shared + static_cast<int64_t>(a.num_kv_heads) * private_wgs * a.num_seqs *
+                                       ((a.num_parts + 3) / 4);
+    a.shared_units = static_cast<int32_t>(shared);
+    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kPlain, kBS, true, false, true>),
+                       dim3(static_cast<uint32_t>(total)), dim3(4 * 64), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int64_t shared = a.num_kv_heads * prefix_wgs * a.shared_parts;
+  const int64_t total = shared + static_cast<int64_t>(a.num_kv_heads) * private_wgs * a.num_seqs * a.num_parts;
+  a.shared_units = static_cast<int32_t>(shared);
+  if (a.partition_tokens >= kWideTokens) {
+    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kPlain, kBS, false, false, true>),
+                       dim3(static_cast<uint32_t>(total)), dim3(8 * 64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<M, Tr, D, 4, kChunks, kPlain, kBS, false, false, true>),
+                       dim3(static_cast<uint32_t>(total)), dim3(4 * 64), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+template <class M, class Tr, int D>
+hipError_t launch_prefix_t(const DecodeArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  // float32 tiles at d 128 fill the registers with one chunk already
+  const bool two = group > 16 && !(M::kKBytes == 4 && D == 128);
+  if (a.block_size == 8)
+    return two ? launch_prefix_c<M, Tr, D, 2, 8>(a, stream) : launch_prefix_c<M, Tr, D, 1, 8>(a, stream);
+  return two ? launch_prefix_c<M, Tr, D, 2, 16>(a, stream) : launch_prefix_c<M, Tr, D, 1, 16>(a, stream);
+}
+template <class M, class Tr>
+hipError_t launch_prefix_dim(const DecodeArgs& a, hipStream_t stream) {
+  return a.head_dim == 64 ? launch_prefix_t<M, Tr, 64>(a, stream)
+                          : launch_prefix_t<M, Tr, 128>(a, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
@@ -996,6 +1067,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     case PA_K2_F16: return launch_dim_k2<MmaF16, F16>(a, stream);
     case PA_K2_BF16: return launch_dim_k2<MmaBF16, BF16>(a, stream);
     default: return launch_dim<MmaBF16, BF16>(a, stream);
+  }
+}
+
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.dtype) {
+    case PA_F32: return launch_prefix_dim<MmaF32, F32>(a, stream);
+    case PA_F16: return launch_prefix_dim<MmaF16, F16>(a, stream);
+    default: return launch_prefix_dim<MmaBF16, BF16>(a, stream);
   }
 }
 

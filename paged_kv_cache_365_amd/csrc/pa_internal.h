@@ -32,6 +32,13 @@ struct DecodeArgs {
   float scale;
   int32_t partition_tokens;  // tokens per partition (a multiple of 16)
   int32_t num_parts;         // partitions per sequence in the grid
+  int32_t part_stride;       // partitions per row in the workspace (>= part_offset + num_parts)
+  int32_t part_offset;       // first partition the grid computes
+  // shared-prefix launches: the prefix role covers partitions [0, shared_parts)
+  // of the shared_tokens-token prefix (set by the launcher: shared_units)
+  int32_t shared_parts;
+  int32_t shared_tokens;
+  int32_t shared_units;
   bool write_partials;       // true: o_part/lse_part into the workspace; false: out
   float* o_part;
   float* lse_part;
@@ -40,6 +47,8 @@ struct DecodeArgs {
 
 // Launch the decode kernel chosen for (dtype, head_dim).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Shared-prefix split launch (16-bit or float32 pools, one query token).
+hipError_t launch_decode_shared_prefix(const DecodeArgs& a, hipStream_t stream);
 
 struct ReduceArgs {
   const float* o_part;

@@ -30,7 +30,7 @@ BLOCK_SIZE = 16
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_init_pool", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
-           "pa_verify_decode", "pa_write_kv_k8", "pa_decode_k8", "pa_write_kv_k2", "pa_decode_k2",
+           "pa_verify_decode", "pa_decode_shared_prefix", "pa_write_kv_k8", "pa_decode_k8", "pa_write_kv_k2", "pa_decode_k2",
            "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
            "pa_scatter_blocks", "pa_status_string")
 
@@ -76,6 +76,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_verify_decode.restype = ctypes.c_int
     lib.pa_verify_decode.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                      ctypes.c_float, i32, vp, sz, vp, vp]
+    lib.pa_decode_shared_prefix.restype = ctypes.c_int
+    lib.pa_decode_shared_prefix.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                            ctypes.c_float, i32, i32, vp, sz, vp]
     lib.pa_write_kv_k8.restype = ctypes.c_int
     lib.pa_write_kv_k8.argtypes = [desc, vp, vp, vp, vp, vp, i64p, i32, vp]
     lib.pa_decode_k8.restype = ctypes.c_int
@@ -267,6 +270,24 @@ def pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_
         ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, T, Hq, int(max_context_len),
         float(scale), int(partition_size), _ptr(workspace), ws_bytes, _ptr(out), _stream(stream)))
+
+
+def pa_decode_shared_prefix(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                            scale: float, prefix_tokens: int, partition_size: int, workspace,
+                            stream=None) -> None:
+    """Split decode (partials into ``workspace``, merged by pa_reduce) of a batch
+    whose tables all start with the same prefix_tokens / bs blocks."""
+    chk = _Args("pa_decode_shared_prefix")
+    desc = pool_desc(k_pool, v_pool, chk)
+    _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, workspace, None, 3)
+    B, Hq, _ = q.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    chk.on_gpu()
+    _check("pa_decode_shared_prefix", load().pa_decode_shared_prefix(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), B, Hq, int(max_context_len),
+        float(scale), int(prefix_tokens), int(partition_size), _ptr(workspace), ws_bytes,
+        _stream(stream)))
 
 
 def pa_write_kv_k8(k_pool, v_pool, k_scale, k_new, v_new, slot_mapping, stream=None) -> None:
@@ -499,4 +520,20 @@ def k2_attention(q, k_pool, v_pool, k_scale, k_zero, block_tables, context_lens,
     else:
         pa_decode_k2(q, k_pool, v_pool, k_scale, k_zero, block_tables, context_lens,
                      max_context_len, scale, 0, None, out, stream)
+    return out
+
+
+def shared_prefix_attention(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                            scale: float, prefix_tokens: int, partition_size: int, workspace=None,
+                            out=None, stream=None):
+    """out = pa_decode_shared_prefix + pa_reduce.  q is [B][H_q][d]."""
+    if out is None:
+        out = torch.empty_like(q)
+    B, Hq, D = q.shape
+    if workspace is None:
+        n = pa_decode_workspace_bytes(B, Hq, D, max_context_len, partition_size)
+        workspace = torch.empty(n // 4, dtype=torch.float32, device=q.device)
+    pa_decode_shared_prefix(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
+                            prefix_tokens, partition_size, workspace, stream)
+    pa_reduce(workspace, context_lens, B, Hq, D, max_context_len, partition_size, out, stream)
     return out

@@ -209,3 +209,23 @@ def test_k2_calls_reject_bad_arguments(lib):
     assert d8(ctypes.byref(k2), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 1, 4, 40, 0.125, 0,
               None, 0, FAKE, None) == pa.PA_ERR_UNSUPPORTED
     assert lib.pa_reduce(FAKE, FAKE, 2, 4, 64, 40, 16, pa.PA_K2_BF16, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+
+
+def test_shared_prefix_call_rejects_bad_arguments(lib):
+    bf = _desc(dtype=pa.PA_BF16)
+    k8 = _desc(dtype=pa.PA_K8_BF16)
+    sp = lib.pa_decode_shared_prefix
+    need = pa.pa_decode_workspace_bytes(2, 4, 64, 40, 16)
+
+    def call(desc=bf, prefix=16, P=16, maxlen=40, ws=FAKE, ws_bytes=need, tables=FAKE):
+        return sp(ctypes.byref(desc), FAKE, FAKE, FAKE, tables, 4, FAKE, 2, 4, maxlen, 0.125,
+                  prefix, P, ws, ws_bytes, None)
+    assert call(desc=k8) == pa.PA_ERR_UNSUPPORTED
+    assert call(P=0) == pa.PA_ERR_INVALID_ARG               # always split
+    assert call(prefix=0) == pa.PA_ERR_INVALID_ARG
+    assert call(prefix=24, P=16) == pa.PA_ERR_INVALID_ARG   # not a whole number of partitions
+    assert call(prefix=48) == pa.PA_ERR_INVALID_ARG         # longer than max_context_len
+    assert call(P=8) == pa.PA_ERR_INVALID_ARG               # partitions are multiples of 16
+    assert call(tables=None) == pa.PA_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 4) == pa.PA_ERR_WORKSPACE
+    assert call(ws=None) == pa.PA_ERR_WORKSPACE
