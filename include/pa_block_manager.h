@@ -147,6 +147,16 @@ pa_status pa_bm_fill_tables(const pa_block_manager* bm, const int64_t* seq_ids, 
 pa_status pa_bm_sort_longest_first(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
                                    int64_t* out_ids);
 
+/* The shared prefix of a decode batch: *prefix_blocks = the number of leading
+ * block-table entries that every sequence of seq_ids has in common (the same
+ * physical blocks, e.g. a system prompt matched by pa_bm_match_prefix or
+ * blocks inherited by pa_bm_fork), capped at the full blocks every context
+ * covers (floor(min context length / block_size)).  Such a batch satisfies the
+ * contract of pa_decode_shared_prefix with prefix_tokens = *prefix_blocks *
+ * block_size (or any multiple of the partition size below it).  n = 0 gives 0. */
+pa_status pa_bm_common_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                              int32_t* prefix_blocks);
+
 pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* stats);
 
 /* Reference count of a physical block (-1 when out of range). */

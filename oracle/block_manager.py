@@ -246,3 +246,19 @@ def sort_longest_first(model: BlockManagerModel, seqs):
     """The batch ordered by context length, longest first; equal lengths keep
     their order."""
     return sorted(seqs, key=lambda s: -model.lens[s])
+
+
+def common_prefix(model: BlockManagerModel, seqs):
+    """Leading table entries every sequence of the batch shares (the same
+    physical blocks), capped at the full blocks every context covers."""
+    seqs = list(seqs)
+    if not seqs:
+        return 0
+    tables = [model.tables[s] for s in seqs]
+    k = min(len(tables[0]), min(model.lens[s] for s in seqs) // model.bs)
+    for t in tables[1:]:
+        j = 0
+        while j < k and j < len(t) and t[j] == tables[0][j]:
+            j += 1
+        k = j
+    return k

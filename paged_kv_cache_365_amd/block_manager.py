@@ -18,7 +18,7 @@ EXPORTS = ("pa_bm_create", "pa_bm_destroy", "pa_bm_add_seq", "pa_bm_match_prefix
            "pa_bm_append", "pa_bm_append_step", "pa_bm_fork", "pa_bm_free_seq",
            "pa_bm_swap_out", "pa_bm_swap_in", "pa_bm_get_table", "pa_bm_fill_tables",
            "pa_bm_get_stats", "pa_bm_refcount", "pa_bm_blocks_needed",
-           "pa_bm_sort_longest_first")
+           "pa_bm_sort_longest_first", "pa_bm_common_prefix")
 
 
 class Stats(ctypes.Structure):
@@ -56,6 +56,7 @@ def _lib():
             "pa_bm_refcount": [vp, i32],
             "pa_bm_blocks_needed": [vp, i64, i32],
             "pa_bm_sort_longest_first": [vp, vp, i32, vp],
+            "pa_bm_common_prefix": [vp, vp, i32, vp],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -184,6 +185,16 @@ class BlockManager:
         pa._check("pa_bm_sort_longest_first", self._lib.pa_bm_sort_longest_first(
             self._h, _p(ids), int(ids.size), _p(out)))
         return out[: ids.size]
+
+    def common_prefix(self, seqs) -> int:
+        """Leading table entries every sequence of ``seqs`` shares, capped at the
+        full blocks every context covers (the prefix pa_decode_shared_prefix can
+        take)."""
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        k = ctypes.c_int32()
+        pa._check("pa_bm_common_prefix", self._lib.pa_bm_common_prefix(
+            self._h, _p(ids), int(ids.size), ctypes.byref(k)))
+        return int(k.value)
 
     def stats(self) -> dict:
         st = Stats()

@@ -411,6 +411,31 @@ pa_status pa_bm_sort_longest_first(const pa_block_manager* bm, const int64_t* se
   return PA_OK;
 }
 
+pa_status pa_bm_common_prefix(const pa_block_manager* bm, const int64_t* seq_ids, int32_t n,
+                              int32_t* prefix_blocks) {
+  if (!valid_bm(bm) || n < 0 || !prefix_blocks || (n > 0 && !seq_ids)) return PA_ERR_INVALID_ARG;
+  std::vector<const Seq*> ss(static_cast<size_t>(n));
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seq_ids[i]);
+    if (it == bm->seqs.end()) return PA_ERR_INVALID_ARG;
+    ss[i] = &it->second;
+  }
+  int32_t k = 0;
+  if (n > 0) {
+    int32_t min_len = ss[0]->len;
+    for (const Seq* q : ss) min_len = std::min(min_len, q->len);
+    k = std::min(static_cast<int32_t>(ss[0]->table.size()), min_len / bm->bs);
+    for (int32_t i = 1; i < n && k > 0; ++i) {
+      const std::vector<int32_t>& t = ss[i]->table;
+      int32_t j = 0;
+      while (j < k && j < static_cast<int32_t>(t.size()) && t[j] == ss[0]->table[j]) ++j;
+      k = j;
+    }
+  }
+  *prefix_blocks = k;
+  return PA_OK;
+}
+
 pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* st) {
   if (!valid_bm(bm) || !st) return PA_ERR_INVALID_ARG;
   int32_t used = 0;

@@ -254,3 +254,44 @@ def test_serving_trace(seed, dtype, hkv, hq, d, bs):
     st = srv.bm.stats()
     assert st["prefix_hit_blocks"] > 0 and st["cow_copies"] > 0
     assert srv.checks >= 9
+
+
+@pytest.mark.parametrize("dtype,bs,P", [("bf16", 16, 32), ("f16", 8, 16)])
+def test_system_prompt_batch_through_shared_prefix_call(dtype, bs, P):
+    """A batch behind one system prompt, built by the block manager (prompt
+    blocks matched from its cache, private tokens appended), K/V written by
+    pa_write_kv at the manager's slots; pa_bm_common_prefix gives the prefix
+    pa_decode_shared_prefix takes, and its output equals the oracle's over the
+    manager's own tables."""
+    rng = np.random.default_rng(77)
+    hkv, hq, d, nb = 2, 8, 64, 96
+    prompt = list(range(500, 500 + 4 * bs + 5))            # 4 full blocks + 5 tokens
+    bm = BlockManager(nb, bs)
+    ks, vs = wl.pool_shapes(nb, hkv, d, dtype, block_size=bs)
+    kp = wl.normal(rng, ks, dtype)
+    vp = wl.normal(rng, vs, dtype)
+    tk, tv = to_torch(kp, dtype, DEV), to_torch(vp, dtype, DEV)
+    seqs = [0, 1, 2, 3, 4]
+    for s, extra in zip(seqs, [3, 40, 1, 75, 20]):
+        toks = prompt + [s] * extra
+        bm.add_seq(s, True)
+        matched = bm.match_prefix(s, toks)
+        slots, copies = bm.append(s, len(toks) - matched, toks[matched:])
+        assert copies is None
+        kn = wl.normal(rng, (len(slots), hkv, d), dtype)
+        vn = wl.normal(rng, (len(slots), hkv, d), dtype)
+        pa.pa_write_kv(tk, tv, to_torch(kn, dtype, DEV), to_torch(vn, dtype, DEV),
+                       torch.from_numpy(np.asarray(slots, np.int64)).to(DEV))
+    k = bm.common_prefix(seqs)
+    assert k == 4
+    prefix = (k * bs) // P * P
+    tables, lens = bm.fill_tables(seqs, 16)
+    q = wl.normal(rng, (len(seqs), hq, d), dtype)
+    tq = to_torch(q, dtype, DEV)
+    scale = float(np.float32(d ** -0.5))
+    out = pa.shared_prefix_attention(tq, tk, tv, torch.from_numpy(tables).to(DEV),
+                                     torch.from_numpy(lens).to(DEV), int(lens.max()), scale,
+                                     prefix, P)
+    torch.cuda.synchronize()
+    want = oracle.paged_decode(q, to_numpy(tk), to_numpy(tv), tables, lens, scale, dtype)
+    assert np.abs(widen_f32(out) - want).max() <= 2e-2

@@ -81,6 +81,9 @@ BM_MUTATIONS = {
     "stack_fifo": [("return self.free.pop()", "return self.free.pop(0)")],
     "fork_no_incref": [("        for b in self.tables[child]:\n            self.ref[b] += 1\n", "")],
     "needed_without_cow": [("        return new + cow\n", "        return new\n")],
+    "common_prefix_uncapped": [("    k = min(len(tables[0]), min(model.lens[s] for s in seqs) // model.bs)\n",
+                                "    k = len(tables[0])\n")],
+    "common_prefix_first_pair": [("    for t in tables[1:]:\n        j = 0", "    for t in tables[1:2]:\n        j = 0")],
     "swap_in_shares": [("            b = self._take()\n            self.ref[b] = 1\n            table.append(b)\n        self.tables[seq] = table",
                         "            b = self._take()\n            self.ref[b] = 1\n            table.append(0)\n        self.tables[seq] = table")],
 }
