@@ -2,7 +2,8 @@
 
 Every entry point is asynchronous, allocates nothing, synchronises nothing and
 records no memset, so a decode step (KV append, split decode, log-sum-exp
-merge) can be captured once and replayed.  Each replay here is separated by
+merge; also with 2-bit keys, and the shared-prefix call) can be captured once
+and replayed.  Each replay here is separated by
 the test's own eager work and synchronisations, gets new inputs written into
 the captured buffers, and must match the eager result bit for bit.  Two
 independent decodes on two streams must also match their single-stream
@@ -101,3 +102,89 @@ def test_two_streams_match_single_stream():
         torch.cuda.synchronize()
         for r, o in zip(ref, outs):
             assert torch.equal(r, o)
+
+
+def _replays_match_eager(step, fill_inputs, out, reps=4):
+    """Capture ``step`` once; each replay on fresh inputs must equal the same
+    step run eagerly right after it, bit for bit."""
+    fill_inputs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        fill_inputs()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(got, out), f"replay {rep} differs from the eager step"
+        del junk
+
+
+def test_two_bit_key_step_graph_replays_match_eager():
+    """2-bit keys: quantised append, split decode and merge in one graph."""
+    dtype, P = "bf16", 32
+    lens = [40, 130, 257, 16]
+    w = wl.make_random_case(992, num_seqs=4, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                            dtype=dtype, lens=lens)
+    d = upload(w, DEV)
+    words, step_s, zero = wl.k2_inputs(w, 993)
+    kp = torch.from_numpy(words.view(np.int32)).to(DEV)
+    ts = torch.from_numpy(step_s).to(DEV)
+    tz = torch.from_numpy(zero).to(DEV)
+    B, Hq, D = d.q.shape
+    rng = np.random.default_rng(994)
+    q = torch.empty((B, 1, Hq, D), dtype=d.q.dtype, device=DEV)
+    k_new = torch.empty((B, 2, D), dtype=d.q.dtype, device=DEV)
+    v_new = torch.empty_like(k_new)
+    slots = torch.tensor([int(w.block_tables[s, (L - 1) // 16]) * 16 + (L - 1) % 16
+                          for s, L in enumerate(lens)], dtype=torch.int64, device=DEV)
+    out = torch.empty_like(q)
+    n = pa.pa_decode_workspace_bytes(B, Hq, D, w.max_context_len, P)
+    ws = torch.empty(n // 4, dtype=torch.float32, device=DEV)
+
+    def fill_inputs():
+        q.copy_(to_torch(wl.normal(rng, (B, 1, Hq, D), dtype), dtype, DEV))
+        k_new.copy_(to_torch(wl.normal(rng, (B, 2, D), dtype), dtype, DEV))
+        v_new.copy_(to_torch(wl.normal(rng, (B, 2, D), dtype), dtype, DEV))
+
+    def step(stream):
+        pa.pa_write_kv_k2(kp, d.v_pool, ts, tz, k_new, v_new, slots, stream)
+        pa.pa_decode_k2(q, kp, d.v_pool, ts, tz, d.block_tables, d.context_lens,
+                        w.max_context_len, w.scale, P, ws, None, stream)
+        pa.pa_reduce(ws, d.context_lens, B, Hq, D, w.max_context_len, P, out, stream)
+
+    _replays_match_eager(step, fill_inputs, out)
+
+
+def test_shared_prefix_step_graph_replays_match_eager():
+    """The shared-prefix call and its merge in one graph."""
+    dtype, P, prefix = "bf16", 64, 128
+    w = wl.make_random_case(996, num_seqs=6, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                            dtype=dtype, lens=[128, 200, 500, 129, 300, 700], prefix_tokens=prefix)
+    d = upload(w, DEV)
+    B, Hq, D = d.q.shape
+    rng = np.random.default_rng(997)
+    q = torch.empty_like(d.q)
+    out = torch.empty_like(q)
+    n = pa.pa_decode_workspace_bytes(B, Hq, D, w.max_context_len, P)
+    ws = torch.empty(n // 4, dtype=torch.float32, device=DEV)
+
+    def fill_inputs():
+        q.copy_(to_torch(wl.normal(rng, (B, Hq, D), dtype), dtype, DEV))
+
+    def step(stream):
+        pa.pa_decode_shared_prefix(q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
+                                   w.max_context_len, w.scale, prefix, P, ws, stream)
+        pa.pa_reduce(ws, d.context_lens, B, Hq, D, w.max_context_len, P, out, stream)
+
+    _replays_match_eager(step, fill_inputs, out)
