@@ -210,13 +210,15 @@ def test_k2_70b_gqa_4k_sampled():
         assert np.abs(got[s] - want).max() <= TOL, s
 
 
-@pytest.mark.parametrize("cfg,P,seqs", [(4, 512, (0, 3)), (1, 0, (0, 13, 31))])
-def test_k2_full_size_workloads(cfg, P, seqs):
+@pytest.mark.parametrize("cfg,P,seqs,bs", [(4, 512, (0, 3), 16), (1, 0, (0, 13, 31), 16),
+                                           (2, 0, (5, 62), 8)])
+def test_k2_full_size_workloads(cfg, P, seqs, bs):
     """2-bit keys over the long-context workload (4 x 32768 tokens, 64/8 heads)
     split into its own 512-token partitions and merged by pa_reduce, and over
     the 7B-style ragged MHA batch (32 x U[512, 4096] tokens, 32/32 heads,
-    f16) unsplit; whole sequences against the oracle."""
-    w = wl.make_config(cfg)
+    f16) unsplit, and the 70B-style batch cut into 8-token blocks; whole
+    sequences against the oracle."""
+    w = wl.make_config(cfg, block_size=bs)
     words, step, zero = wl.k2_inputs(w, 2060 + cfg)
     dw = upload(w, DEV)
     q = w.q[:, None]
