@@ -9,7 +9,7 @@ Default workload: 70B-style GQA decode -- 64 sequences, 64 query heads over 8
 KV heads, head_dim 128, bf16 KV, every context 4096 tokens, 16-token blocks,
 shuffled block tables.  Prints one JSON line on stdout; progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--config 2]
 """
 from __future__ import annotations
 
@@ -143,7 +143,7 @@ def copy_bandwidth(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload index 0..4 (default: 70B GQA 4K)")
     ap.add_argument("--partition", type=int, default=None, help="override the partition size")
