@@ -801,6 +801,14 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
     }
   }
 
+  // Here partials are stored with the streaming hint: they are read once, by
+  // the merge kernel, and plain stores that stay in L2 cost this launch more
+  // than their bytes, all waves storing at once at the end (70B batch at
+  // 512-token partitions: decode 182.3 -> 172-176 us; 163 us with no stores at
+  // all; 32K batch 88.4 -> 86-87.6 us).  Rows stored whole through LDS, or
+  // written through to memory (agent- or system-scope stores), measured no
+  // better or worse; the merged stores of the LDS path below stay plain (the
+  // hint cost the shared-prefix batch 69 -> 73 us there).
   if constexpr (kWavePart || kLds) {
     // every row of this wave lives in this wave alone (its own partition, or
     // its own chunk of the workgroup's rows): normalise in registers and write
@@ -808,19 +816,20 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
     for (int c = 0; c < kChunks; ++c) {
       const int rho = row0 + 16 * c + r;
       const float ls = sum_over_q(lsum[c]);  // all lanes take part
-      if (rho >= rows) continue;
       const bool seen = m[c] != -INFINITY;
       const float inv = seen ? 1.f / ls : 0.f;
       const size_t row = (static_cast<size_t>(s) * T + rho / group) * a.num_q_heads +
                          g * group + rho % group;
       if (a.write_partials) {
-        float* op = a.o_part + (row * a.part_stride + part) * D + 4 * qg;
-#pragma unroll
-        for (int cb = 0; cb < kColBlocks; ++cb)
-          *reinterpret_cast<f32x4*>(op + 16 * cb) = acc[c][cb] * inv;
-        if (qg == 0)
+        if (qg == 0 && rho < rows)
           a.lse_part[row * a.part_stride + part] = seen ? (m[c] + __log2f(ls)) * kLn2 : -INFINITY;
-      } else {
+        if (rho < rows) {
+          float* op = a.o_part + (row * a.part_stride + part) * D + 4 * qg;
+#pragma unroll
+          for (int cb = 0; cb < kColBlocks; ++cb)
+            __builtin_nontemporal_store(acc[c][cb] * inv, reinterpret_cast<f32x4*>(op + 16 * cb));
+        }
+      } else if (rho < rows) {
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb)
 #pragma unroll
