@@ -232,3 +232,33 @@ def test_k2_full_size_workloads(cfg, P, seqs, bs):
         want = qk.paged_decode_k2(q[s:s + 1], words, w.v_pool, w.block_tables[s:s + 1],
                                   w.context_lens[s:s + 1], w.scale, step, zero, w.dtype)[0, 0]
         assert np.abs(got[s] - want).max() <= TOL, (w.name, s)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_k2_random_sweep(seed):
+    """Random shapes drawn from the seed: value type, head_dim, query heads per
+    KV head (1 to 16), draft length (1 to 8), partition size (0, 16, 48, 64),
+    block size and ragged lengths."""
+    rng = np.random.default_rng(4000 + seed)
+    dtype = ["bf16", "f16"][seed % 2]
+    d = [64, 128][(seed // 2) % 2]
+    hkv = int(rng.choice([1, 2, 4]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8, 16]))
+    T = int(rng.integers(1, 9))
+    P = int(rng.choice([0, 16, 48, 64]))
+    bs = int(rng.choice([8, 16]))
+    lens = [int(x) for x in rng.integers(1, 200, size=int(rng.integers(1, 6)))]
+    w = wl.make_random_case(4100 + seed, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=d, dtype=dtype, lens=lens, block_size=bs)
+    words, step, zero = wl.k2_inputs(w, 4200 + seed, outlier_columns=1)
+    q = wl.normal(rng, (len(lens), T, hq, d), dtype)
+    dw = upload(w, DEV)
+    out = pa.k2_attention(to_torch(q, dtype, DEV), k2_tensor(words), dw.v_pool, f32_tensor(step),
+                          f32_tensor(zero), dw.block_tables, dw.context_lens, w.max_context_len,
+                          w.scale, partition_size=P)
+    torch.cuda.synchronize()
+    want = qk.paged_decode_k2(q, words, w.v_pool, w.block_tables, w.context_lens, w.scale, step,
+                              zero, dtype)
+    got = widen_f32(out)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL, (dtype, d, hq, hkv, T, P, bs, lens)

@@ -95,3 +95,29 @@ def test_shared_prefix_workload_full_size(P):
                              w.max_context_len, w.scale, partition_size=P)
     torch.cuda.synchronize()
     assert np.abs(got - widen_f32(ref)).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_shared_prefix_random_sweep(seed):
+    """Random shapes drawn from the seed: value type, head_dim, heads, block
+    size, prefix length (a whole number of partitions), partition size and
+    private lengths from 0 to several partitions."""
+    rng = np.random.default_rng(5000 + seed)
+    dtype = ["bf16", "f16", "f32"][seed % 3]
+    D = [64, 128][(seed // 3) % 2]
+    hkv = int(rng.choice([1, 2, 8]))
+    hq = hkv * int(rng.choice([1, 4, 8, 32]))
+    bs = int(rng.choice([8, 16]))
+    P = int(rng.choice([16, 32, 64]))
+    prefix = P * int(rng.integers(1, 4))
+    B = int(rng.integers(1, 10))
+    lens = [prefix + int(x) for x in rng.integers(0, 3 * P, size=B)]
+    w = wl.make_random_case(5100 + seed, num_seqs=B, num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=D, dtype=dtype, lens=lens, prefix_tokens=prefix,
+                            block_size=bs)
+    d = upload(w, DEV)
+    got, _ = run_prefix(w, d, prefix, P)
+    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                               dtype)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype], (dtype, D, hq, hkv, bs, P, prefix, lens)

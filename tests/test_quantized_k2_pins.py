@@ -296,3 +296,27 @@ def test_partial_lse_equals_dense_log_sum_exp():
         for p in range(3):
             xs = x[p * P:min(37, (p + 1) * P)]
             np.testing.assert_allclose(lse[0, h, p], np.log(np.exp(xs).sum()), rtol=0, atol=1e-12)
+
+
+def test_calibrated_range_ends_map_to_the_end_codes():
+    """The sketch of §4.2 (blog.tanteng.space page) divides a channel's range by
+    2^bits - 1: with z = the channel minimum and s = (max - min) / 3, the minimum
+    and the maximum of the calibration keys get codes 0 and 3 and dequantise to
+    themselves (up to the float32 rounding of s), and the middle of the range
+    lies half-way between codes 1 and 2 (rounded to the even one, 2)."""
+    rng = np.random.default_rng(30)
+    K = wl.f64_to_storage(rng.standard_normal((64, 2, 64)) * 2.0, "bf16")
+    Kf = bf16_to_f64(K)
+    lo, hi = Kf.min(axis=0), Kf.max(axis=0)
+    z = lo.astype(np.float32)
+    s = ((hi - lo) / 3).astype(np.float32)
+    codes = qk.quantize_k2(K, s, z, "bf16")
+    at_min = Kf == lo[None]
+    at_max = Kf == hi[None]
+    assert (codes[at_min] == 0).all() and (codes[at_max] == 3).all()
+    kh = qk.dequantize_k2(codes, s, z)
+    np.testing.assert_allclose(kh[at_max], np.broadcast_to(hi, Kf.shape)[at_max], rtol=1e-6)
+    np.testing.assert_array_equal(kh[at_min], np.broadcast_to(lo, Kf.shape)[at_min])
+    mid = wl.f64_to_storage(np.array([[[-1.0 + 1.5 * 0.5]]]), "bf16")      # z=-1, s=0.5: u = 1.5
+    assert qk.quantize_k2(mid, np.full((1, 1), 0.5, np.float32), np.full((1, 1), -1.0, np.float32),
+                          "bf16")[0, 0, 0] == 2
