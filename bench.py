@@ -118,7 +118,15 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0, verify
     T = 1 if verify_q is None else verify_q.shape[1]
     key_bytes = 1 if k8 is not None else (0.25 if k2 is not None else None)
     gbps = w.algorithmic_bytes(query_tokens=T, key_bytes=key_bytes) * frac / dt / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    host = {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "cpu_model": model}
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": host,
             "sample": f"{done_seqs} sequences ({frac:.2f} passes over all {B} sequences x "
                       f"{w.num_q_heads} heads of the workload), numpy float64, one thread, "
                       f"{dt:.1f} s",
