@@ -32,15 +32,15 @@ def _gpu():
     pa.load()  # raises when libpa.so is missing: no fallback path exists
 
 
-_CONFIGS = {}
+_WORKLOAD_CACHE = {}
 
 
 def config(i):
-    if i not in _CONFIGS:
-        _CONFIGS.clear()  # hold one large workload at a time
+    if i not in _WORKLOAD_CACHE:
+        _WORKLOAD_CACHE.clear()  # hold one large workload at a time
         w = wl.make_config(i)
-        _CONFIGS[i] = (w, upload(w, DEV))
-    return _CONFIGS[i]
+        _WORKLOAD_CACHE[i] = (w, upload(w, DEV))
+    return _WORKLOAD_CACHE[i]
 
 
 def run_decode(d, partition_size, out_dtype=None):
