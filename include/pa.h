@@ -209,27 +209,32 @@ pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_
 /* Split decode of a batch whose block tables all start with the same
  * prefix_tokens / bs physical blocks (a shared system prompt: §2.3 of the
  * blog.tanteng.space page, blocks referenced by several tables).  The result
- * is exactly pa_decode's in split mode with partition_size: the same
- * partials in the same workspace layout, merged afterwards by pa_reduce with
- * the same partition_size.  The partitions of the prefix are computed once per
- * KV head for the query rows of every sequence together (each prefix tile is
- * read from memory once for the batch instead of once per sequence); the rest
- * of each context is computed per sequence as pa_decode does.
+ * is exactly pa_decode's (or pa_decode_k8's / pa_decode_k2's) in split mode
+ * with partition_size: the same partials in the same workspace layout, merged
+ * afterwards by pa_reduce with the same partition_size.  The partitions of the
+ * prefix are computed once per KV head for the query rows of every sequence
+ * together (each prefix tile is read from memory once for the batch instead of
+ * once per sequence); the rest of each context is computed per sequence as
+ * pa_decode does.
  *
+ * Any pool type: k_scale is the int8 or 2-bit keys' float32 [H_kv][d] scales
+ * (steps), k_zero the 2-bit keys' zero points, both as for pa_decode_k8 /
+ * pa_decode_k2 and null for the other pools (PA_ERR_INVALID_ARG when a
+ * quantised pool lacks them, PA_ERR_UNSUPPORTED when a plain pool gets them).
  * prefix_tokens: a positive multiple of partition_size, at most
  * max_context_len; partition_size > 0, a multiple of 16.  One query token per
- * sequence (q [num_seqs][num_q_heads][head_dim]); f32, f16 or bf16 pools
- * (quantised pools: PA_ERR_UNSUPPORTED).  Caller's contract on device data
- * (not checked): every table's first prefix_tokens / bs entries equal table
- * row 0's, and every context_lens[s] >= prefix_tokens; otherwise the prefix
- * partitions use row 0's blocks and all prefix_tokens tokens anyway (a wrong
- * result, never an out-of-bounds access). */
+ * sequence (q [num_seqs][num_q_heads][head_dim]).  Caller's contract on device
+ * data (not checked): every table's first prefix_tokens / bs entries equal
+ * table row 0's, and every context_lens[s] >= prefix_tokens; otherwise the
+ * prefix partitions use row 0's blocks and all prefix_tokens tokens anyway (a
+ * wrong result, never an out-of-bounds access). */
 pa_status pa_decode_shared_prefix(const pa_pool_desc* pool, const void* q, const void* k_pool,
-                                  const void* v_pool, const int32_t* block_tables,
-                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                  int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                                  float scale, int32_t prefix_tokens, int32_t partition_size,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                  const void* v_pool, const float* k_scale, const float* k_zero,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len, float scale,
+                                  int32_t prefix_tokens, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
 
 /* Quantised key cache (§4.2 of the blog.tanteng.space page: keys quantised
  * per channel, values kept in 16-bit; "KV Cache量化" of the ybb.press page:

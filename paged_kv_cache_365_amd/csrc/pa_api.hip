@@ -258,17 +258,17 @@ pa_status pa_decode_k8(const pa_pool_desc* pool, const void* q, const void* k_po
 }
 
 pa_status pa_decode_shared_prefix(const pa_pool_desc* pool, const void* q, const void* k_pool,
-                                  const void* v_pool, const int32_t* block_tables,
-                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                  int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                                  float scale, int32_t prefix_tokens, int32_t partition_size,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (pool && is_quantized(pool->dtype)) return PA_ERR_UNSUPPORTED;
+                                  const void* v_pool, const float* k_scale, const float* k_zero,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_context_len, float scale,
+                                  int32_t prefix_tokens, int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
   if (partition_size <= 0 || prefix_tokens <= 0 || prefix_tokens % partition_size != 0 ||
       prefix_tokens > max_context_len)
     return PA_ERR_INVALID_ARG;
   // always split: partials into the workspace, merged by pa_reduce
-  return decode_common(pool, q, k_pool, v_pool, nullptr, nullptr, block_tables, max_blocks_per_seq,
+  return decode_common(pool, q, k_pool, v_pool, k_scale, k_zero, block_tables, max_blocks_per_seq,
                        context_lens, num_seqs, 1, num_q_heads, max_context_len, scale,
                        partition_size, workspace, workspace_bytes, nullptr, stream, prefix_tokens);
 }

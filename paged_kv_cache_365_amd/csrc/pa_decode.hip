@@ -1083,6 +1083,14 @@ hipError_t launch_decode_shared_prefix(const DecodeArgs& a, hipStream_t stream) 
   switch (a.dtype) {
     case PA_F32: return launch_prefix_dim<MmaF32, F32>(a, stream);
     case PA_F16: return launch_prefix_dim<MmaF16, F16>(a, stream);
+    case PA_K8_F16: return launch_prefix_dim<MmaK8<MmaF16>, F16>(a, stream);
+    case PA_K8_BF16: return launch_prefix_dim<MmaK8<MmaBF16>, BF16>(a, stream);
+    case PA_K2_F16:
+      return a.head_dim == 64 ? launch_prefix_t<MmaK2<MmaF16, 64>, F16, 64>(a, stream)
+                              : launch_prefix_t<MmaK2<MmaF16, 128>, F16, 128>(a, stream);
+    case PA_K2_BF16:
+      return a.head_dim == 64 ? launch_prefix_t<MmaK2<MmaBF16, 64>, BF16, 64>(a, stream)
+                              : launch_prefix_t<MmaK2<MmaBF16, 128>, BF16, 128>(a, stream);
     default: return launch_prefix_dim<MmaBF16, BF16>(a, stream);
   }
 }

@@ -47,7 +47,7 @@ struct DecodeArgs {
 
 // Launch the decode kernel chosen for (dtype, head_dim).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// Shared-prefix split launch (16-bit or float32 pools, one query token).
+// Shared-prefix split launch (any pool type, one query token).
 hipError_t launch_decode_shared_prefix(const DecodeArgs& a, hipStream_t stream);
 
 struct ReduceArgs {

@@ -77,7 +77,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_verify_decode.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                      ctypes.c_float, i32, vp, sz, vp, vp]
     lib.pa_decode_shared_prefix.restype = ctypes.c_int
-    lib.pa_decode_shared_prefix.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+    lib.pa_decode_shared_prefix.argtypes = [desc, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32,
                                             ctypes.c_float, i32, i32, vp, sz, vp]
     lib.pa_write_kv_k8.restype = ctypes.c_int
     lib.pa_write_kv_k8.argtypes = [desc, vp, vp, vp, vp, vp, i64p, i32, vp]
@@ -274,17 +274,21 @@ def pa_verify_decode(q, k_pool, v_pool, block_tables, context_lens, max_context_
 
 def pa_decode_shared_prefix(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
                             scale: float, prefix_tokens: int, partition_size: int, workspace,
-                            stream=None) -> None:
+                            stream=None, k_scale=None, k_zero=None) -> None:
     """Split decode (partials into ``workspace``, merged by pa_reduce) of a batch
-    whose tables all start with the same prefix_tokens / bs blocks."""
+    whose tables all start with the same prefix_tokens / bs blocks.  Quantised
+    key pools take their float32 [H_kv][d] ``k_scale`` (and 2-bit keys ``k_zero``)."""
     chk = _Args("pa_decode_shared_prefix")
     desc = pool_desc(k_pool, v_pool, chk)
+    chk("k_scale", k_scale, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
+    chk("k_zero", k_zero, torch.float32, 2, (desc.num_kv_heads, desc.head_dim))
     _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, workspace, None, 3)
     B, Hq, _ = q.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     chk.on_gpu()
     _check("pa_decode_shared_prefix", load().pa_decode_shared_prefix(
-        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(k_zero),
+        _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, Hq, int(max_context_len),
         float(scale), int(prefix_tokens), int(partition_size), _ptr(workspace), ws_bytes,
         _stream(stream)))
@@ -525,7 +529,7 @@ def k2_attention(q, k_pool, v_pool, k_scale, k_zero, block_tables, context_lens,
 
 def shared_prefix_attention(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
                             scale: float, prefix_tokens: int, partition_size: int, workspace=None,
-                            out=None, stream=None):
+                            out=None, stream=None, k_scale=None, k_zero=None):
     """out = pa_decode_shared_prefix + pa_reduce.  q is [B][H_q][d]."""
     if out is None:
         out = torch.empty_like(q)
@@ -534,6 +538,6 @@ def shared_prefix_attention(q, k_pool, v_pool, block_tables, context_lens, max_c
         n = pa_decode_workspace_bytes(B, Hq, D, max_context_len, partition_size)
         workspace = torch.empty(n // 4, dtype=torch.float32, device=q.device)
     pa_decode_shared_prefix(q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale,
-                            prefix_tokens, partition_size, workspace, stream)
+                            prefix_tokens, partition_size, workspace, stream, k_scale, k_zero)
     pa_reduce(workspace, context_lens, B, Hq, D, max_context_len, partition_size, out, stream)
     return out

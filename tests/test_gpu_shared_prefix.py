@@ -121,3 +121,35 @@ def test_shared_prefix_random_sweep(seed):
                                dtype)
     assert np.isfinite(got).all()
     assert np.abs(got - want).max() <= TOL[dtype], (dtype, D, hq, hkv, bs, P, prefix, lens)
+
+
+@pytest.mark.parametrize("kind,dtype,D,hq,hkv,bs,P,prefix", [
+    ("k8", "bf16", 128, 32, 8, 16, 32, 64), ("k8", "f16", 64, 8, 2, 8, 16, 48),
+    ("k2", "bf16", 128, 32, 8, 16, 64, 128), ("k2", "f16", 64, 16, 4, 8, 16, 32),
+])
+def test_shared_prefix_quantised_keys(kind, dtype, D, hq, hkv, bs, P, prefix):
+    """The shared-prefix call over int8 and 2-bit key pools equals the oracle's
+    attention over the dequantised keys."""
+    from oracle import quantized_kv as qk
+    lens = [prefix, prefix + 1, prefix + 70, prefix + 2 * P + 5, prefix + 9]
+    w = wl.make_random_case(5300 + len(kind) + D, num_seqs=len(lens), num_q_heads=hq,
+                            num_kv_heads=hkv, head_dim=D, dtype=dtype, lens=lens,
+                            prefix_tokens=prefix, block_size=bs)
+    d = upload(w, DEV)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+    if kind == "k8":
+        codes, scale = wl.k8_inputs(w, 5400, outlier_columns=2)
+        kp, ks, kz = torch.from_numpy(codes).to(DEV), f32(scale), None
+        want = qk.paged_decode_k8(w.q[:, None], codes, w.v_pool, w.block_tables, w.context_lens,
+                                  w.scale, scale, dtype)[:, 0]
+    else:
+        words, step, zero = wl.k2_inputs(w, 5500, outlier_columns=2)
+        kp, ks, kz = torch.from_numpy(words.view(np.int32)).to(DEV), f32(step), f32(zero)
+        want = qk.paged_decode_k2(w.q[:, None], words, w.v_pool, w.block_tables, w.context_lens,
+                                  w.scale, step, zero, dtype)[:, 0]
+    out = pa.shared_prefix_attention(d.q, kp, d.v_pool, d.block_tables, d.context_lens,
+                                     w.max_context_len, w.scale, prefix, P, k_scale=ks, k_zero=kz)
+    torch.cuda.synchronize()
+    got = widen_f32(out)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= TOL[dtype]

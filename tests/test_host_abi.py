@@ -217,10 +217,14 @@ def test_shared_prefix_call_rejects_bad_arguments(lib):
     sp = lib.pa_decode_shared_prefix
     need = pa.pa_decode_workspace_bytes(2, 4, 64, 40, 16)
 
-    def call(desc=bf, prefix=16, P=16, maxlen=40, ws=FAKE, ws_bytes=need, tables=FAKE):
-        return sp(ctypes.byref(desc), FAKE, FAKE, FAKE, tables, 4, FAKE, 2, 4, maxlen, 0.125,
+    def call(desc=bf, prefix=16, P=16, maxlen=40, ws=FAKE, ws_bytes=need, tables=FAKE, ks=None,
+             kz=None):
+        return sp(ctypes.byref(desc), FAKE, FAKE, FAKE, ks, kz, tables, 4, FAKE, 2, 4, maxlen, 0.125,
                   prefix, P, ws, ws_bytes, None)
-    assert call(desc=k8) == pa.PA_ERR_UNSUPPORTED
+    assert call(desc=k8) == pa.PA_ERR_INVALID_ARG            # int8 keys need their scales
+    assert call(ks=FAKE) == pa.PA_ERR_UNSUPPORTED            # a plain pool takes none
+    assert call(desc=_desc(dtype=pa.PA_K2_BF16), ks=FAKE) == pa.PA_ERR_INVALID_ARG  # and zero points
+    assert call(desc=k8, ks=FAKE + 4) == pa.PA_ERR_MISALIGNED
     assert call(P=0) == pa.PA_ERR_INVALID_ARG               # always split
     assert call(prefix=0) == pa.PA_ERR_INVALID_ARG
     assert call(prefix=24, P=16) == pa.PA_ERR_INVALID_ARG   # not a whole number of partitions
