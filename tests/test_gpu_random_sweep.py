@@ -1,0 +1,107 @@
+"""A broad random parity sweep: every attention entry point of the C ABI
+(pa_decode, pa_verify_decode, pa_decode_k8, pa_decode_k2,
+pa_decode_shared_prefix, each followed by pa_reduce when split) on shapes drawn
+from the seed, against the fp64 oracle (tolerances of
+``tests/test_gpu_parity.py``).
+
+Each seed draws: the entry point (cycled), the value type (float32 / f16 / bf16;
+f16 / bf16 for quantised keys), head_dim 64 or 128, 1-8 KV heads, 1-64 query
+heads per KV head, a 1-16 token draft for the multi-token calls (capped so a
+KV head holds at most 512 query rows), 8- or 16-token blocks, the partition
+size (0 = unsplit, 16 to 128 tokens), 1-6 sequences and their lengths (up to
+40, 200 or 600 tokens; a prefix of 1-2 partitions for the shared-prefix call),
+with one outlier key channel scaled x10 for the quantised pools.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quantized_kv as qk
+from paged_kv_cache_365_amd import pa
+from paged_kv_cache_365_amd import workloads as wl
+from paged_kv_cache_365_amd.device import to_torch, upload, widen_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
+KINDS = ["decode", "verify", "k8", "k2", "prefix"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    pa.load()
+
+
+def draw(seed):
+    rng = np.random.default_rng(90000 + seed)
+    kind = KINDS[seed % len(KINDS)]
+    dtype = str(rng.choice(["bf16", "f16"] if kind in ("k8", "k2") else ["bf16", "f16", "f32"]))
+    d = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    T = int(rng.integers(1, 17)) if kind in ("verify", "k8", "k2") else 1
+    while T * g > 512:
+        T = max(1, T // 2)
+    bs = int(rng.choice([8, 16]))
+    P = int(rng.choice([0, 16, 32, 64, 128]))
+    B = int(rng.integers(1, 7))
+    maxl = int(rng.choice([40, 200, 600]))
+    prefix = 0
+    if kind == "prefix":
+        P = int(rng.choice([16, 32, 64]))
+        prefix = P * int(rng.integers(1, 3))
+        lens = [prefix + int(x) for x in rng.integers(0, maxl, size=B)]
+    else:
+        lens = [int(x) for x in rng.integers(1, maxl + 1, size=B)]
+    while B * hkv * g * T * max(lens) * d > 6e7 and g > 1:  # keep the oracle to a fraction of a second
+        g //= 2
+    return rng, kind, dtype, d, hkv, hkv * g, T, bs, P, prefix, lens
+
+
+@pytest.mark.parametrize("seed", range(150))
+def test_random_sweep(seed):
+    rng, kind, dtype, d, hkv, hq, T, bs, P, prefix, lens = draw(seed)
+    case = (kind, dtype, d, hkv, hq, T, bs, P, prefix, lens)
+    print("case", seed, case, flush=True)
+    w = wl.make_random_case(91000 + seed, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=d, dtype=dtype, lens=lens, prefix_tokens=prefix,
+                            block_size=bs)
+    dw = upload(w, DEV)
+    if kind in ("decode", "prefix"):
+        q, tq = w.q, dw.q
+    else:
+        q = wl.normal(rng, (len(lens), T, hq, d), dtype)
+        tq = to_torch(q, dtype, DEV)
+    args = (dw.block_tables, dw.context_lens, w.max_context_len, w.scale)
+    if kind == "decode":
+        out = pa.paged_attention(tq, dw.k_pool, dw.v_pool, *args, partition_size=P)
+        want = oracle.paged_decode(q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                                   w.scale, dtype)
+    elif kind == "verify":
+        out = pa.verify_attention(tq, dw.k_pool, dw.v_pool, *args, partition_size=P)
+        want = oracle.paged_verify(q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                                   w.scale, dtype)
+    elif kind == "k8":
+        codes, sc = wl.k8_inputs(w, 92000 + seed, outlier_columns=1)
+        out = pa.k8_attention(tq, torch.from_numpy(codes).to(DEV), dw.v_pool,
+                              torch.from_numpy(sc).to(DEV), *args, partition_size=P)
+        want = qk.paged_decode_k8(q, codes, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                                  sc, dtype)
+    elif kind == "k2":
+        words, st, zp = wl.k2_inputs(w, 93000 + seed, outlier_columns=1)
+        out = pa.k2_attention(tq, torch.from_numpy(words.view(np.int32)).to(DEV), dw.v_pool,
+                              torch.from_numpy(st).to(DEV), torch.from_numpy(zp).to(DEV), *args,
+                              partition_size=P)
+        want = qk.paged_decode_k2(q, words, w.v_pool, w.block_tables, w.context_lens, w.scale,
+                                  st, zp, dtype)
+    else:
+        out = pa.shared_prefix_attention(tq, dw.k_pool, dw.v_pool, *args, prefix, P)
+        want = oracle.paged_decode(q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
+                                   w.scale, dtype)
+    torch.cuda.synchronize()
+    got = widen_f32(out)
+    assert np.isfinite(got).all(), case
+    err = np.abs(got - want).max()
+    assert err <= TOL[dtype], f"{case}: max-abs {err:.3e}"
