@@ -233,3 +233,20 @@ def test_shared_prefix_call_rejects_bad_arguments(lib):
     assert call(tables=None) == pa.PA_ERR_INVALID_ARG
     assert call(ws_bytes=need - 4) == pa.PA_ERR_WORKSPACE
     assert call(ws=None) == pa.PA_ERR_WORKSPACE
+
+
+def test_missing_library_raises(tmp_path):
+    """No fallback: a missing shared library is an error, not a CPU path."""
+    with pytest.raises(RuntimeError, match="missing"):
+        pa.load(str(tmp_path / "libpa.so"))
+
+
+def test_package_never_reaches_the_oracle():
+    """The product package imports nothing from oracle/ (only the tests, the
+    smoke check and the benchmark's CPU baseline may)."""
+    pkg = os.path.join(ROOT, "paged_kv_cache_365_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
