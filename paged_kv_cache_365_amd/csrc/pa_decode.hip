@@ -893,7 +893,11 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
 // evenly); shorter ones get 4.  2-bit keys always get 4: a step carries 4.5 KiB
 // instead of 8, and three 4-wave workgroups per compute unit keep more of them
 // in flight than one of 8 (measured on the 70B batch: 97.1 -> 92.9 us; ring
-// depths 3 and 4 changed nothing).
+// depths 3 and 4 changed nothing).  Waves holding two row chunks (17 to 32 rows
+// per KV head) get 4 as well: the same waves fit a compute unit as two 4-wave
+// workgroups as one of 8, and the smaller ones start and finish independently
+// and merge four waves' results instead of eight (70B batch verifying a
+// 4-token draft: 178 -> 171 us; with int8 keys 148 -> 137 us).
 constexpr int kWideTokens = 4096;
 
 // One wave per partition needs at least this many partitions per sequence and
@@ -927,9 +931,9 @@ hipError_t launch_cs(const DecodeArgs& a, int wgs, hipStream_t stream) {
     return hipGetLastError();
   }
   const dim3 grid(units * a.num_parts);
-  // Four chunks hold 64 rows of state per lane: only 4 waves per workgroup fit
-  // them without spilling.
-  if constexpr (kChunks < 4) {
+  // Only one-chunk waves take 8-wave workgroups (two chunks: see kWideTokens;
+  // four hold 64 rows of state per lane, which only 4 waves fit unspilled).
+  if constexpr (kChunks == 1) {
     if (M::kKBits != 2 && a.partition_tokens >= kWideTokens) {
       hipLaunchKernelGGL((decode_kernel<M, Tr, D, 8, kChunks, kShared, kBS, false>), grid,
                          dim3(8 * 64), 0, stream, a);
