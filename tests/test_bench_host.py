@@ -1,0 +1,83 @@
+"""Host-side logic of bench.py (no GPU): the algorithmic byte count of a decode
+launch, the stored HBM-traffic lookup and its invalidation when the decode
+kernel's sources change, and the one-GPU limit."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+from paged_kv_cache_365_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("bs", [16, 8])
+@pytest.mark.parametrize("partition", [0, 32])
+def test_decode_kernel_bytes_by_hand(bs, partition):
+    """K and V of every live token, q (and out when unsplit), one 4-byte table
+    entry per live block of bs tokens, one 4-byte length per sequence."""
+    lens = [1, 16, 17, 40]
+    w = wl.make_random_case(7, num_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                            dtype="bf16", lens=lens, block_size=bs)
+    kv = sum(lens) * 2 * 2 * 64 * 2
+    qo = 4 * 8 * 64 * 2
+    table = 4 * sum((L + bs - 1) // bs for L in lens)
+    want = kv + qo * (1 if partition else 2) + table + 4 * 4
+    assert bench.decode_kernel_bytes(w, partition) == want
+    if partition == 0:  # unsplit, the launch moves the workload's whole algorithmic bytes
+        assert want == w.algorithmic_bytes()
+    # a T-token draft reads the same K/V once and moves q and out T times
+    assert bench.decode_kernel_bytes(w, partition, query_tokens=3) == want + 2 * qo * (
+        1 if partition else 2)
+    # int8 keys: 1 byte per key element plus a float32 scale per (KV head, channel)
+    assert bench.decode_kernel_bytes(w, partition, key_bytes=1) == (
+        want - sum(lens) * 2 * 64 * 1 + 4 * 2 * 64)
+
+
+def test_stored_traffic_entries_name_their_summaries():
+    rec = json.load(open(os.path.join(ROOT, "profiles", "pa_decode_traffic.json")))
+    assert rec
+    for workload, e in rec.items():
+        summary = os.path.join(ROOT, e["summary"])
+        assert os.path.exists(summary), workload
+        text = open(summary).read()
+        assert e["kernel_source_hash"] in text, workload
+        assert e["hbm_bytes_per_launch"] == e["fetch_bytes"] + e["write_bytes"], workload
+        assert e["fetch_factor"] > 0 and e["write_factor"] > 0
+
+
+def test_stored_traffic_lookup(monkeypatch):
+    rec = json.load(open(os.path.join(ROOT, "profiles", "pa_decode_traffic.json")))
+    workload, e = next(iter(rec.items()))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: e["kernel_source_hash"])
+    assert bench.stored_traffic(workload, e["partition_size"]) == e["hbm_bytes_per_launch"]
+    assert bench.stored_traffic(workload, e["partition_size"] + 16) is None
+    assert bench.stored_traffic("no-such-workload", 0) is None
+    # counters taken on other kernel sources are not reported
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.stored_traffic(workload, e["partition_size"]) is None
+
+
+def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch):
+    h = bench.kernel_source_hash()
+    assert len(h) == 16 and h == bench.kernel_source_hash()
+    csrc = tmp_path / "paged_kv_cache_365_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    for name in bench.DECODE_SOURCES:
+        src = os.path.join(ROOT, "paged_kv_cache_365_amd", "csrc", name)
+        (csrc / name).write_bytes(open(src, "rb").read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.kernel_source_hash() == h
+    (csrc / "pa_common.h").write_bytes((csrc / "pa_common.h").read_bytes() + b"\n")
+    assert bench.kernel_source_hash() != h
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
