@@ -2,7 +2,10 @@
 inputs, through the C ABI.
 
 Tolerances (max-abs against the fp64 oracle): 1e-5 for float32 KV, 2e-2 for
-float16 / bfloat16 KV (float32 accumulation inside the kernels).  Gather indices,
+float16 / bfloat16 KV (float32 accumulation inside the kernels).  The workloads
+at full size, and the long contexts, are compared on every output element, and
+also against the output-scaled bound of ``parity_bounds`` (the kernel's error
+budget), which a dropped or misrouted block does not meet.  Gather indices,
 KV append and pool fill are compared bit for bit.  Invariants that hold exactly
 for the method (relabelling physical blocks, shared-prefix rows, a one-token
 context, run-to-run determinism) are checked bit for bit on the GPU output.
@@ -15,6 +18,7 @@ import oracle
 from paged_kv_cache_365_amd import pa, tuning
 from paged_kv_cache_365_amd import workloads as wl
 from paged_kv_cache_365_amd.device import TORCH_DTYPE, to_numpy, to_torch, upload, widen_f32
+from parity_bounds import assert_parity
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
@@ -33,14 +37,25 @@ def _gpu():
 
 
 _WORKLOAD_CACHE = {}
+_ORACLE_CACHE = {}
 
 
 def config(i):
     if i not in _WORKLOAD_CACHE:
         _WORKLOAD_CACHE.clear()  # hold one large workload at a time
+        _ORACLE_CACHE.clear()
         w = wl.make_config(i)
         _WORKLOAD_CACHE[i] = (w, upload(w, DEV))
     return _WORKLOAD_CACHE[i]
+
+
+def oracle_full(i):
+    """The oracle's output on every (sequence, head) row of workload i."""
+    w, _ = config(i)
+    if i not in _ORACLE_CACHE:
+        _ORACLE_CACHE[i] = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables,
+                                               w.context_lens, w.scale, w.dtype)
+    return _ORACLE_CACHE[i]
 
 
 def run_decode(d, partition_size, out_dtype=None):
@@ -64,15 +79,6 @@ def split_workspace(ws, B, Hq, D, n_parts):
     n = B * Hq * n_parts
     return ws[: n * D].reshape(B, Hq, n_parts, D).astype(np.float64), \
         ws[n * D: n * D + n].reshape(B, Hq, n_parts).astype(np.float64)
-
-
-def sample_pairs(w, n, seed=0):
-    rng = np.random.default_rng(seed)
-    B, H = w.num_seqs, w.num_q_heads
-    pairs = {(0, h) for h in range(H)} | {(B - 1, 0), (B - 1, H - 1)}
-    while len(pairs) < n + H:
-        pairs.add((int(rng.integers(B)), int(rng.integers(H))))
-    return sorted(pairs)
 
 
 def assert_close(got, want, tol, what):
@@ -221,7 +227,7 @@ def test_long_context_full_oracle(P):
     out, _ = run_decode(dw, P)
     want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
                                w.scale, "bf16")
-    assert_close(widen_f32(out), want, TOL["bf16"], f"131072 tokens P{P}")
+    assert_parity(widen_f32(out), want, "bf16", f"131072 tokens P{P}")
 
 
 # ---------------------------------------------------------------------------
@@ -229,33 +235,21 @@ def test_long_context_full_oracle(P):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("i", range(5))
 def test_decode_config(i):
+    """Every output element of each workload at full size, in the launch the
+    benchmark times, against the oracle."""
     w, d = config(i)
     P = tuning.partition_for(w)
-    out, _ = run_decode(d, P)
-    got = widen_f32(out)
-    if i == 0:
-        want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens,
-                                   w.scale, w.dtype)
-        assert_close(got, want, TOL[w.dtype], w.name)
-        return
-    pairs = sample_pairs(w, 48, seed=i)
-    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
-                               w.dtype, pairs=pairs)
-    idx = tuple(np.array(pairs).T)
-    assert_close(got[idx], want[idx], TOL[w.dtype], f"{w.name} P{P}")
-    assert np.isfinite(got).all()
+    got = widen_f32(run_decode(d, P)[0])
+    assert_parity(got, oracle_full(i), w.dtype, f"{w.name} P{P} (all {w.num_seqs * w.num_q_heads} rows)")
 
 
 @pytest.mark.parametrize("i,P", [(2, 0), (2, 512), (4, 0), (4, 2048), (1, 256), (3, 128)])
 def test_decode_config_other_partitions(i, P):
-    """Split and unsplit runs of the same workload agree with the oracle and with each other."""
+    """Split and unsplit runs of the same workload agree with the oracle on every
+    element and with each other."""
     w, d = config(i)
     got = widen_f32(run_decode(d, P)[0])
-    pairs = sample_pairs(w, 16, seed=100 + i)
-    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
-                               w.dtype, pairs=pairs)
-    idx = tuple(np.array(pairs).T)
-    assert_close(got[idx], want[idx], TOL[w.dtype], f"{w.name} P{P}")
+    assert_parity(got, oracle_full(i), w.dtype, f"{w.name} P{P} (all rows)")
     ref = widen_f32(run_decode(d, tuning.partition_for(w))[0])
     assert np.abs(got - ref).max() <= TOL[w.dtype]
 
