@@ -69,6 +69,7 @@
 
 #include "pa_common.h"
 #include "pa_internal.h"
+#include "pa_units.h"
 
 namespace pa {
 namespace {
@@ -337,43 +338,10 @@ __device__ __forceinline__ float sum_over_q(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Work unit of a workgroup.  The grid is one-dimensional; units are numbered
-// sibling-fastest, then partition, KV head, sequence: n = ((s * H_kv + g) *
-// parts + p) * wgs + w, where the wgs siblings w split the rows of one
-// (s, g, p) and read the same K/V tiles.  Workgroups are handed to the 8 XCDs
-// round-robin (workgroup i to XCD i mod 8), and each XCD has its own L2, so
-// when there are siblings the ids are permuted to put all siblings of a unit
-// on one XCD, dispatched back to back: the tiles the first one brings into
-// that L2 serve the others.  Without siblings the numbering is the identity.
-struct Unit {
-  int sibling, part, kv_head, seq;
-};
-
 // physical blocks of one 16-token step (b == a for 16-token blocks)
 struct Phys {
   int a, b;
 };
-__device__ __forceinline__ Unit unit_of(int id, int total, int wgs, int parts, int kv_heads) {
-  constexpr int kXcds = 8;
-  int n = id;
-  if (wgs > 1) {
-    const int span = kXcds * wgs;
-    const int whole = total / span * span;  // the tail past whole multiples keeps its ids
-    if (id < whole) {
-      const int xcd = id % kXcds;
-      const int slot = id / kXcds;  // position in this XCD's dispatch order
-      n = ((slot / wgs) * kXcds + xcd) * wgs + slot % wgs;
-    }
-  }
-  Unit u;
-  u.sibling = n % wgs;
-  n /= wgs;
-  u.part = n % parts;
-  n /= parts;
-  u.kv_head = n % kv_heads;
-  u.seq = n / kv_heads;
-  return u;
-}
 
 // Wavefronts per SIMD the register allocation must leave room for (512
 // registers per lane and SIMD): the ring of kDepth steps, the accumulators and
