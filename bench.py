@@ -30,7 +30,7 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-DECODE_SOURCES = ("pa_decode.hip", "pa_common.h", "pa_internal.h")
+DECODE_SOURCES = ("pa_decode.hip", "pa_common.h", "pa_internal.h", "pa_units.h")
 
 
 def kernel_source_hash() -> str:
@@ -78,19 +78,15 @@ def decode_kernel_bytes(w, partition: int, query_tokens: int = 1, key_bytes=None
             4 * w.num_seqs + scales)
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0, verify_q=None,
-                 k8=None, k2=None):
-    """The fp64 oracle, single-threaded, on the same workload: whole passes over
-    every sequence until about ``min_seconds`` have elapsed (bounded by
-    ``max_seconds``; the last pass may stop early).  ``verify_q`` [B][T][H_q][d]:
-    time the verify oracle over that draft instead; ``k8`` = (codes, scales):
-    the int8-key oracle; ``k2`` = (words, steps, zero points): the 2-bit-key
-    oracle."""
+def _oracle_pass(w, min_seconds, max_seconds, threads, verify_q=None, k8=None, k2=None):
+    """Whole passes of the fp64 oracle over every sequence of the workload, with
+    ``threads`` BLAS threads, until about ``min_seconds`` have elapsed (bounded by
+    ``max_seconds``; the last pass may stop early).  Returns (sequences, seconds)."""
     import oracle
     from oracle import quantized_kv
     from threadpoolctl import threadpool_limits
     B = w.num_seqs
-    with threadpool_limits(1):
+    with threadpool_limits(threads):
         t0 = time.perf_counter()
         done_seqs = 0
         while time.perf_counter() - t0 < min_seconds:
@@ -114,24 +110,40 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_seconds: float = 30.0, verify
                 done_seqs += 1
                 if time.perf_counter() - t0 > max_seconds:
                     break
-        dt = time.perf_counter() - t0
-    frac = done_seqs / B
+        return done_seqs, time.perf_counter() - t0
+
+
+def cpu_baseline(w, min_seconds: float = 8.0, max_seconds: float = 25.0, verify_q=None,
+                 k8=None, k2=None):
+    """The fp64 oracle on the same workload, timed twice: with BLAS threads set to
+    every host core this process may use (the reported value), and with one
+    thread.  ``verify_q`` [B][T][H_q][d]: time the verify oracle over that draft
+    instead; ``k8`` = (codes, scales): the int8-key oracle; ``k2`` = (words,
+    steps, zero points): the 2-bit-key oracle."""
+    B = w.num_seqs
     T = 1 if verify_q is None else verify_q.shape[1]
     key_bytes = 1 if k8 is not None else (0.25 if k2 is not None else None)
-    gbps = w.algorithmic_bytes(query_tokens=T, key_bytes=key_bytes) * frac / dt / 1e9
+    nbytes = w.algorithmic_bytes(query_tokens=T, key_bytes=key_bytes)
+    cores = len(os.sched_getaffinity(0))
+    legs = {}
+    for name, threads in (("all_cores", cores), ("one_thread", 1)):
+        done, dt = _oracle_pass(w, min_seconds, max_seconds, threads, verify_q, k8, k2)
+        legs[name] = {
+            "value": round(nbytes * done / B / dt / 1e9, 4), "cores": threads,
+            "tokens_per_s": round(done * T / dt, 3),
+            "sample": f"{done} sequences ({done / B:.2f} passes over all {B} sequences x "
+                      f"{w.num_q_heads} heads of the workload), numpy float64, BLAS threads "
+                      f"{threads}, {dt:.1f} s"}
     model = None
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
     except OSError:
         pass
-    host = {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
-            "cpu_model": model}
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle", "host": host,
-            "sample": f"{done_seqs} sequences ({frac:.2f} passes over all {B} sequences x "
-                      f"{w.num_q_heads} heads of the workload), numpy float64, one thread, "
-                      f"{dt:.1f} s",
-            "tokens_per_s": round(done_seqs * T / dt, 3)}
+    host = {"cpu_count": os.cpu_count(), "affinity": cores, "cpu_model": model}
+    rec = dict(legs["all_cores"])
+    rec.update({"unit": "GB/s", "kind": "oracle", "host": host, "one_thread": legs["one_thread"]})
+    return rec
 
 
 def copy_bandwidth(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
@@ -147,6 +159,41 @@ def copy_bandwidth(torch, nbytes: int = 1 << 30, reps: int = 10) -> float:
     dt = (time.perf_counter() - t0) / reps
     del src, dst
     return 2 * nbytes / dt / 1e9
+
+
+def time_launches(torch, stream, fn, reps: int = 20) -> float:
+    """Mean seconds of one fn() launch over ``reps`` back-to-back launches
+    (HIP events on the launch stream)."""
+    fn()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps * 1e-3
+
+
+def achievable(torch, pa, w, d, stream, nbytes: int = 1 << 30) -> dict:
+    """Read rates measured in the same run: a plain streaming read of ``nbytes``
+    (pa_probe_read) and, for 16-bit pools of 16-token blocks, the K/V tile reads
+    of the decode call with nothing computed (pa_probe_read_tiles)."""
+    out = {}
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(2048 * 4, dtype=torch.int32, device="cuda")
+    t = time_launches(torch, stream, lambda: pa.pa_probe_read(src, sink, stream))
+    out["stream_read_gbps"] = round(nbytes / t / 1e9, 1)
+    out["stream_read_bytes"] = nbytes
+    del src
+    if w.dtype in ("f16", "bf16") and w.block_size == 16:
+        sink = torch.empty(w.num_seqs * w.num_kv_heads * 8, dtype=torch.int32, device="cuda")
+        t = time_launches(torch, stream, lambda: pa.pa_probe_read_tiles(
+            d.k_pool, d.v_pool, d.block_tables, d.context_lens, d.max_context_len, sink, stream))
+        out["decode_tile_reads_gbps"] = round(w.kv_bytes_logical() / t / 1e9, 1)
+        out["decode_tile_reads_us"] = round(t * 1e6, 2)
+    return out
 
 
 def main() -> int:
@@ -177,6 +224,8 @@ def main() -> int:
                     help="time the speculative-decoding verify call over a T-token draft "
                          "(pa_verify_decode) instead of single-token decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the read probes (streaming read, the decode's tile reads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (for counter calibration)")
     args = ap.parse_args()
@@ -380,6 +429,14 @@ def main() -> int:
         rec["unique_gbps"] = round(rec["unique_bytes_per_step"] / (ms_per_step * 1e-3) / 1e9, 2)
     if copy_gbps is not None:
         rec["device_copy_gbps"] = round(copy_gbps, 1)
+    if not args.no_achievable:
+        ach = achievable(torch, pa, w, d, stream)
+        if "decode_tile_reads_gbps" in ach and not (k8 or k2):
+            # the decode kernel's own KV rate against the same reads with no compute
+            kv_rate = w.kv_bytes_logical() / (decode_ms * 1e-3) / 1e9
+            ach["decode_over_tile_reads"] = round(kv_rate / ach["decode_tile_reads_gbps"], 4)
+        rec["roofline"]["achievable"] = ach
+        log(f"achievable: {ach}")
     del d, out, ws
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -108,9 +108,9 @@ typedef struct pa_pool_desc {
 /* Fill every element of both pools: fill = 0 writes +0.0, fill = 1 writes a
  * quiet NaN (used to prove that unreferenced blocks are never read; an int8
  * key pool gets -128, a code no write produces; a 2-bit key pool, where every
- * bit pattern is a code, gets all ones, code 3).  A pool
- * that has just been taken from the allocator (the fixed-capacity block pool of
- * §2.3 of the tanteng.space page). */
+ * bit pattern is a code, gets all ones, code 3).  Meant for a pool just taken
+ * from the allocator, before any block of it is written (the fixed-capacity
+ * block pool of §2.3 of the blog.tanteng.space page). */
 pa_status pa_init_pool(const pa_pool_desc* pool, void* k_pool, void* v_pool, int32_t fill,
                        hipStream_t stream);
 
@@ -189,10 +189,14 @@ pa_status pa_verify_decode(const pa_pool_desc* pool, const void* q, const void* 
  *   out[s][h] = sum_p exp(lse_p - LSE) o_p,
  * over the ceil(context_lens[s] / partition_size) partitions sequence s has.
  * Exact because the softmax normaliser can be streamed (§4.2 of the
- * ialgorithm.me page).  out is [num_seqs][num_q_heads][head_dim] in out_dtype. */
-pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,
-                    int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                    int32_t partition_size, int32_t out_dtype, void* out, hipStream_t stream);
+ * ialgorithm.me page).  out is [num_seqs][num_q_heads][head_dim] in out_dtype.
+ * workspace_bytes is the size of the workspace buffer: PA_ERR_WORKSPACE when it
+ * is below pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ * max_context_len, partition_size) (the merge would read past it). */
+pa_status pa_reduce(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_context_len, int32_t partition_size, int32_t out_dtype, void* out,
+                    hipStream_t stream);
 
 /* The gather indices pa_decode uses, computed by the same device function:
  * slot_ids[s][t] = block_tables[s][t / bs] * bs + t % bs for t < context_lens[s]
@@ -323,6 +327,30 @@ pa_status pa_gather_blocks(const pa_pool_desc* pool, const void* k_pool, const v
 pa_status pa_scatter_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool,
                             const int32_t* block_ids, int32_t n, const void* k_src,
                             const void* v_src, hipStream_t stream);
+
+/* Measurement probes (not part of the attention): the achievable read rates
+ * the decode kernel's HBM roofline is read against.  Decode attention is bound
+ * by moving K/V from HBM to the compute units (§4.1 of the ialgorithm.me page,
+ * §3.1 of the blog.tanteng.space page), so these read exactly that and compute
+ * nothing.  Each folds what it reads into one XOR word per wavefront, written
+ * to `sink` (device memory, caller-owned), so no load can be dropped.
+ *
+ * pa_probe_read: reads `bytes` (a positive multiple of 16) at `src` (16-byte
+ *   aligned) with 16-byte streaming loads, grid-stride, over sink_words / 4
+ *   workgroups of 256 threads; sink holds sink_words 32-bit words (a positive
+ *   multiple of 4).
+ * pa_probe_read_tiles: reads the K and V tiles pa_decode (unsplit) reads for the
+ *   same pool, tables and lengths, in its order and with its loads: one
+ *   workgroup of 8 wavefronts per (sequence, KV head), wavefront w reads the
+ *   16-token blocks w, w + 8, ... through the block table.  16-bit pools of
+ *   16-token blocks, head_dim 64 or 128; physical ids and lengths are clamped
+ *   as in pa_decode.  sink holds num_seqs * num_kv_heads * 8 words. */
+pa_status pa_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t sink_words,
+                        hipStream_t stream);
+pa_status pa_probe_read_tiles(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, uint32_t* sink, hipStream_t stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* pa_status_string(pa_status status);

@@ -323,14 +323,18 @@ pa_status pa_write_kv_k2(const pa_pool_desc* pool, void* k_pool, void* v_pool, c
                                          pool->dtype, stream));
 }
 
-pa_status pa_reduce(const void* workspace, const int32_t* context_lens, int32_t num_seqs,
-                    int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                    int32_t partition_size, int32_t out_dtype, void* out, hipStream_t stream) {
+pa_status pa_reduce(const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_context_len, int32_t partition_size, int32_t out_dtype, void* out,
+                    hipStream_t stream) {
   if (!workspace || !context_lens || !out) return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || num_q_heads <= 0 || max_context_len < 0) return PA_ERR_INVALID_ARG;
   if (partition_size <= 0 || partition_size % pa::kStep != 0) return PA_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (elem_bytes(out_dtype) == 0 || is_quantized(out_dtype)) return PA_ERR_UNSUPPORTED;
+  if (workspace_bytes < pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                  partition_size))
+    return PA_ERR_WORKSPACE;
   if (!aligned(workspace, 16) || !aligned(out, 16) || !aligned(context_lens, 4))
     return PA_ERR_MISALIGNED;
   // one 64-lane wavefront per 32 output columns of a row: the threads must fit a 1-D grid

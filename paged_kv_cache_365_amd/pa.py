@@ -32,12 +32,18 @@ BLOCK_SIZE = 16
 EXPORTS = ("pa_init_pool", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
            "pa_verify_decode", "pa_decode_shared_prefix", "pa_write_kv_k8", "pa_decode_k8", "pa_write_kv_k2", "pa_decode_k2",
            "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
-           "pa_scatter_blocks", "pa_status_string")
+           "pa_scatter_blocks", "pa_probe_read", "pa_probe_read_tiles", "pa_status_string")
+
+
+STATUS_NAMES = {PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG",
+                PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED", PA_ERR_MISALIGNED: "PA_ERR_MISALIGNED",
+                PA_ERR_WORKSPACE: "PA_ERR_WORKSPACE", PA_ERR_HIP: "PA_ERR_HIP",
+                PA_ERR_NO_SPACE: "PA_ERR_NO_SPACE"}
 
 
 class PAError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn} returned {pa_status_string(status)} ({status})")
+        super().__init__(f"{fn} returned {STATUS_NAMES.get(status, 'PA_ERR_UNKNOWN')} ({status})")
         self.status = status
 
 
@@ -90,7 +96,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_decode_k2.argtypes = [desc, vp, vp, vp, vp, vp, vp, i32, vp, i32, i32, i32, i32,
                                  ctypes.c_float, i32, vp, sz, vp, vp]
     lib.pa_reduce.restype = ctypes.c_int
-    lib.pa_reduce.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.pa_reduce.argtypes = [vp, sz, vp, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.pa_debug_slot_ids.restype = ctypes.c_int
     lib.pa_debug_slot_ids.argtypes = [vp, i32, vp, i32, i32, i32, i32, vp, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
@@ -99,6 +105,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_gather_blocks.argtypes = [desc, vp, vp, vp, i32, vp, vp, vp]
     lib.pa_scatter_blocks.restype = ctypes.c_int
     lib.pa_scatter_blocks.argtypes = [desc, vp, vp, vp, i32, vp, vp, vp]
+    lib.pa_probe_read.restype = ctypes.c_int
+    lib.pa_probe_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.pa_probe_read_tiles.restype = ctypes.c_int
+    lib.pa_probe_read_tiles.argtypes = [desc, vp, vp, vp, i32, vp, i32, i32, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -372,9 +382,14 @@ def pa_reduce(workspace, context_lens, num_seqs: int, num_q_heads: int, head_dim
     if isinstance(out, torch.Tensor) and out.numel() != num_seqs * num_q_heads * head_dim:
         raise ValueError(f"pa_reduce: out holds {out.numel()} elements, expected "
                          f"{num_seqs} x {num_q_heads} x {head_dim}")
+    ws_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+        workspace.numel() * workspace.element_size()
+    if isinstance(workspace, int):   # a raw device address: the caller vouches for its size
+        ws_bytes = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                             partition_size)
     chk.on_gpu()
     _check("pa_reduce", load().pa_reduce(
-        _ptr(workspace), _ptr(context_lens), num_seqs, num_q_heads, head_dim,
+        _ptr(workspace), ws_bytes, _ptr(context_lens), num_seqs, num_q_heads, head_dim,
         int(max_context_len), int(partition_size), TORCH_TO_PA.get(out.dtype, -1), _ptr(out),
         _stream(stream)))
 
@@ -431,6 +446,34 @@ def pa_scatter_blocks(k_pool, v_pool, block_ids, k_src, v_src, stream=None) -> N
     _check("pa_scatter_blocks", load().pa_scatter_blocks(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
         _ptr(k_src), _ptr(v_src), _stream(stream)))
+
+
+def pa_probe_read(src, sink, stream=None) -> None:
+    """Streaming read of the whole of ``src`` (any contiguous device tensor whose
+    size is a multiple of 16 bytes); ``sink`` int32 [4 * workgroups]."""
+    chk = _Args("pa_probe_read")
+    chk("src", src)
+    chk("sink", sink, torch.int32, 1)
+    chk.on_gpu()
+    _check("pa_probe_read", load().pa_probe_read(_ptr(src), src.numel() * src.element_size(),
+                                                 _ptr(sink), int(sink.numel()), _stream(stream)))
+
+
+def pa_probe_read_tiles(k_pool, v_pool, block_tables, context_lens, max_context_len: int, sink,
+                        stream=None) -> None:
+    """The K/V tile reads of an unsplit pa_decode over the same pool and tables;
+    ``sink`` int32 [num_seqs * num_kv_heads * 8]."""
+    chk = _Args("pa_probe_read_tiles")
+    desc = pool_desc(k_pool, v_pool, chk)
+    chk("context_lens", context_lens, torch.int32, 1)
+    B = int(context_lens.shape[0])
+    chk("block_tables", block_tables, torch.int32, 2, (B, None))
+    chk("sink", sink, torch.int32, 1, (B * desc.num_kv_heads * 8,))
+    chk.on_gpu()
+    _check("pa_probe_read_tiles", load().pa_probe_read_tiles(
+        ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), B, int(max_context_len), _ptr(sink),
+        _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

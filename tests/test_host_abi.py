@@ -91,13 +91,22 @@ def test_decode_rejects_bad_arguments(lib, kw, status):
 
 def test_reduce_and_other_calls_reject_bad_arguments(lib):
     r = lib.pa_reduce
-    assert r(None, FAKE, 2, 4, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_INVALID_ARG
-    assert r(FAKE, FAKE, 2, 4, 64, 40, 0, pa.PA_F32, FAKE, None) == pa.PA_ERR_INVALID_ARG
-    assert r(FAKE, FAKE, 2, 4, 96, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
-    assert r(FAKE, FAKE, 2, 4, 64, 40, 16, 9, FAKE, None) == pa.PA_ERR_UNSUPPORTED
-    assert r(FAKE + 4, FAKE, 2, 4, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_MISALIGNED
+    BIG = 1 << 40   # workspace bytes large enough for every call below
+    assert r(None, BIG, FAKE, 2, 4, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert r(FAKE, BIG, FAKE, 2, 4, 64, 40, 0, pa.PA_F32, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert r(FAKE, BIG, FAKE, 2, 4, 96, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert r(FAKE, BIG, FAKE, 2, 4, 64, 40, 16, 9, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert r(FAKE + 4, BIG, FAKE, 2, 4, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_MISALIGNED
     # one wavefront per 32 columns of a row: more than a 1-D grid holds is refused
-    assert r(FAKE, FAKE, 1 << 20, 64, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert r(FAKE, BIG, FAKE, 1 << 20, 64, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    # the workspace must hold the partials the arguments name (the merge reads them all)
+    need = lib.pa_decode_workspace_bytes(2, 4, 64, 40, 16)
+    assert need == 2 * 4 * 3 * (64 + 1) * 4
+    assert r(FAKE, need - 1, FAKE, 2, 4, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_WORKSPACE
+    assert r(FAKE, 0, FAKE, 2, 4, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_WORKSPACE
+    # a larger context or more rows than the decode call sized the workspace for
+    assert r(FAKE, need, FAKE, 2, 4, 64, 49, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_WORKSPACE
+    assert r(FAKE, need, FAKE, 2, 8, 64, 40, 16, pa.PA_F32, FAKE, None) == pa.PA_ERR_WORKSPACE
     d = _desc()
     assert lib.pa_init_pool(ctypes.byref(d), None, FAKE, 0, None) == pa.PA_ERR_INVALID_ARG
     assert lib.pa_init_pool(ctypes.byref(d), FAKE, FAKE, 2, None) == pa.PA_ERR_INVALID_ARG
@@ -176,7 +185,8 @@ def test_k8_calls_reject_bad_arguments(lib):
     assert call(ks=FAKE + 4) == pa.PA_ERR_MISALIGNED      # the kernel reads scales 16 bytes at a time
     assert call(T=0) == pa.PA_ERR_INVALID_ARG
     # pa_reduce writes a plain 16-bit output
-    assert lib.pa_reduce(FAKE, FAKE, 2, 4, 64, 40, 16, pa.PA_K8_BF16, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_reduce(FAKE, 1 << 40, FAKE, 2, 4, 64, 40, 16, pa.PA_K8_BF16, FAKE, None) == \
+        pa.PA_ERR_UNSUPPORTED
     assert pa.pa_status_string(pa.PA_OK) == "PA_OK"
 
 
@@ -208,7 +218,8 @@ def test_k2_calls_reject_bad_arguments(lib):
     d8 = lib.pa_decode_k8
     assert d8(ctypes.byref(k2), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 1, 4, 40, 0.125, 0,
               None, 0, FAKE, None) == pa.PA_ERR_UNSUPPORTED
-    assert lib.pa_reduce(FAKE, FAKE, 2, 4, 64, 40, 16, pa.PA_K2_BF16, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert lib.pa_reduce(FAKE, 1 << 40, FAKE, 2, 4, 64, 40, 16, pa.PA_K2_BF16, FAKE, None) == \
+        pa.PA_ERR_UNSUPPORTED
 
 
 def test_shared_prefix_call_rejects_bad_arguments(lib):
@@ -250,3 +261,23 @@ def test_package_never_reaches_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+
+
+def test_read_probes_reject_bad_arguments(lib):
+    """The measurement probes check their arguments before any launch."""
+    p = lib.pa_probe_read
+    assert p(None, 1024, FAKE, 8, None) == pa.PA_ERR_INVALID_ARG
+    assert p(FAKE, 0, FAKE, 8, None) == pa.PA_ERR_INVALID_ARG
+    assert p(FAKE, 1000, FAKE, 8, None) == pa.PA_ERR_INVALID_ARG     # not a multiple of 16
+    assert p(FAKE, 1024, FAKE, 6, None) == pa.PA_ERR_INVALID_ARG     # 4 words per workgroup
+    assert p(FAKE + 8, 1024, FAKE, 8, None) == pa.PA_ERR_MISALIGNED
+    t = lib.pa_probe_read_tiles
+    bf = _desc(dtype=pa.PA_BF16, d=128)
+    assert t(None, FAKE, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert t(ctypes.byref(bf), FAKE, FAKE, FAKE, 4, FAKE, 0, 40, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert t(ctypes.byref(bf), FAKE, FAKE, FAKE, 2, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    f32 = _desc(dtype=pa.PA_F32)
+    assert t(ctypes.byref(f32), FAKE, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    bs8 = _desc(dtype=pa.PA_BF16, bs=8)
+    assert t(ctypes.byref(bs8), FAKE, FAKE, FAKE, 8, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert t(ctypes.byref(bf), FAKE + 8, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_MISALIGNED
