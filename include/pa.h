@@ -336,9 +336,9 @@ pa_status pa_scatter_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool
  * to `sink` (device memory, caller-owned), so no load can be dropped.
  *
  * pa_probe_read: reads `bytes` (a positive multiple of 16) at `src` (16-byte
- *   aligned) with 16-byte streaming loads, grid-stride, over sink_words / 4
- *   workgroups of 256 threads; sink holds sink_words 32-bit words (a positive
- *   multiple of 4).
+ *   aligned) with 16-byte streaming loads, each wavefront whole contiguous
+ *   4 KiB runs, over sink_words / 4 workgroups of 256 threads; sink holds
+ *   sink_words 32-bit words (a positive multiple of 4).
  * pa_probe_read_tiles: reads the K and V tiles pa_decode (unsplit) reads for the
  *   same pool, tables and lengths, in its order and with its loads: one
  *   workgroup of 8 wavefronts per (sequence, KV head), wavefront w reads the

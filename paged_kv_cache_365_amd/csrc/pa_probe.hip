@@ -26,20 +26,27 @@ __device__ __forceinline__ void sink_wave(uint32_t acc, uint32_t* sink, size_t i
   if ((threadIdx.x & 63) == 0) sink[index] = acc;
 }
 
-// Contiguous 16-byte streaming loads, grid-stride, four in flight per lane.
+// Contiguous streaming read: each wavefront reads whole 4 KiB runs (four
+// 1 KiB loads of 16 bytes per lane, the decode tile's size), runs dealt to the
+// wavefronts round-robin, two runs in flight; the last partial run is read by
+// the first workgroup.
 __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ src, size_t n16,
                                                          uint32_t* __restrict__ sink) {
-  const size_t stride = static_cast<size_t>(gridDim.x) * 256;
-  size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const size_t wave = static_cast<size_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const size_t waves = static_cast<size_t>(gridDim.x) * 4;
+  const size_t runs = n16 / 256;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
-  }
-  for (; i < n16; i += stride) acc ^= fold(__builtin_nontemporal_load(src + i));
+  auto run = [&](size_t k) {
+    const u32x4* p = src + k * 256 + lane;
+    return fold(__builtin_nontemporal_load(p)) ^ fold(__builtin_nontemporal_load(p + 64)) ^
+           fold(__builtin_nontemporal_load(p + 128)) ^ fold(__builtin_nontemporal_load(p + 192));
+  };
+  size_t k = wave;
+  for (; k + waves < runs; k += 2 * waves) acc ^= run(k) ^ run(k + waves);
+  if (k < runs) acc ^= run(k);
+  if (blockIdx.x == 0)
+    for (size_t i = runs * 256 + threadIdx.x; i < n16; i += 256) acc ^= fold(__builtin_nontemporal_load(src + i));
   sink_wave(acc, sink, static_cast<size_t>(blockIdx.x) * 4 + (threadIdx.x >> 6));
 }
 

@@ -17,6 +17,8 @@ from paged_kv_cache_365_amd import pa
 from paged_kv_cache_365_amd import workloads as wl
 from paged_kv_cache_365_amd.device import upload, widen_f32
 
+from parity_bounds import assert_parity
+
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2}
@@ -77,24 +79,29 @@ def test_shared_prefix_random_cases(case):
     assert np.abs(lse_p[live] - wlse[live]).max() <= (1e-5 if dtype == "f32" else 1e-2)
 
 
+_FULL = {}
+
+
 @pytest.mark.parametrize("P", [256, 512, 1024])
 def test_shared_prefix_workload_full_size(P):
     """The shared-prefix workload (128 sequences, 1024-token shared prefix +
-    U[16, 1024] private tokens, 32/8 heads, bf16) at full size: sampled
-    (sequence, head) rows against the oracle, and the whole output against
-    pa_decode's split result at the same partition size."""
-    w = wl.make_config(3)
-    d = upload(w, DEV)
+    U[16, 1024] private tokens, 32/8 heads, bf16) at full size: every
+    (sequence, head) row against the oracle under both parity gates, and the
+    whole output against pa_decode's split result at the same partition size."""
+    if "w" not in _FULL:
+        w = wl.make_config(3)
+        _FULL.update(w=w, d=upload(w, DEV),
+                     want=oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables,
+                                              w.context_lens, w.scale, w.dtype))
+    w, d, want = _FULL["w"], _FULL["d"], _FULL["want"]
     got, _ = run_prefix(w, d, 1024, P)
-    pairs = [(s, h) for s in (0, 1, 63, 127) for h in (0, 5, 31)]
-    want = oracle.paged_decode(w.q, w.k_pool, w.v_pool, w.block_tables, w.context_lens, w.scale,
-                               w.dtype, pairs=pairs)
-    idx = tuple(np.array(pairs).T)
-    assert np.abs(got[idx] - want[idx]).max() <= TOL["bf16"]
+    assert_parity(got, want, "bf16", f"shared-prefix-gqa4 pa_decode_shared_prefix P{P} (all rows)")
     ref = pa.paged_attention(d.q, d.k_pool, d.v_pool, d.block_tables, d.context_lens,
                              w.max_context_len, w.scale, partition_size=P)
     torch.cuda.synchronize()
     assert np.abs(got - widen_f32(ref)).max() <= TOL["bf16"]
+    if P == 1024:
+        _FULL.clear()
 
 
 @pytest.mark.parametrize("seed", range(10))
