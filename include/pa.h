@@ -328,6 +328,29 @@ pa_status pa_scatter_blocks(const pa_pool_desc* pool, void* k_pool, void* v_pool
                             const int32_t* block_ids, int32_t n, const void* k_src,
                             const void* v_src, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): pa_decode
+ * in split mode followed by pa_reduce, with the partials in a fixed device
+ * array of PA_STATIC_SCRATCH_BYTES inside the library instead of a caller
+ * workspace.  Arguments as pa_decode's (16-bit or float32 pools; quantised
+ * pools are PA_ERR_UNSUPPORTED), partition_size > 0, out written as by
+ * pa_reduce; the result is the same bits as pa_decode + pa_reduce with the
+ * same partition_size.  PA_ERR_WORKSPACE when pa_decode_workspace_bytes for
+ * these arguments exceeds PA_STATIC_SCRATCH_BYTES.  Nothing is allocated: each
+ * GPU the library runs on holds one copy of the array until the process ends
+ * (its address is looked up on the first call made with that device current).
+ * Every call on a GPU uses that GPU's one array, so calls that overlap on one
+ * GPU (on different streams, or from several threads) race; calls on one
+ * stream are ordered and safe.  The array keeps the last call's partials; no
+ * call reads a partial it did not write. */
+#define PA_STATIC_SCRATCH_BYTES (32u << 20)
+pa_status pa_decode_split_static(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 float scale, int32_t partition_size, void* out,
+                                 hipStream_t stream);
+
 /* Measurement probes (not part of the attention): the achievable read rates
  * the decode kernel's HBM roofline is read against.  Decode attention is bound
  * by moving K/V from HBM to the compute units (§4.1 of the ialgorithm.me page,

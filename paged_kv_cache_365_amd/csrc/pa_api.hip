@@ -2,6 +2,8 @@
 // Nothing here allocates device memory or synchronises.
 #include <limits.h>
 
+#include <mutex>
+
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -455,6 +457,67 @@ pa_status pa_debug_slot_ids(const int32_t* block_tables, int32_t max_blocks_per_
   if (max_context_len == 0) return PA_OK;
   return from_hip(pa::launch_slot_ids(block_tables, max_blocks_per_seq, context_lens, num_seqs,
                                       max_context_len, num_blocks, block_size, slot_ids, stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Split decode with no allocation: the partials live in a fixed device array.
+// ---------------------------------------------------------------------------
+// One copy per GPU the library runs on, held until the process ends.  Host
+// code never passes `scratch` itself to a kernel or a copy: its host-side name
+// is not a device address.  The address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use).
+pa_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_split_static(const pa_pool_desc* pool, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                 float scale, int32_t partition_size, void* out,
+                                 hipStream_t stream) {
+  pa_status st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (is_quantized(pool->dtype)) return PA_ERR_UNSUPPORTED;
+  if (partition_size <= 0 || partition_size % pa::kStep != 0 || !out) return PA_ERR_INVALID_ARG;
+  const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, pool->head_dim,
+                                                max_context_len, partition_size);
+  if (need == 0) return PA_ERR_INVALID_ARG;
+  if (need > PA_STATIC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != PA_OK) return st;
+  // every partial the merge reads is written by the decode launch first: nothing
+  // left in the array by an earlier call is read
+  st = pa_decode(pool, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                 num_q_heads, max_context_len, scale, partition_size, ws, need, nullptr, stream);
+  if (st != PA_OK) return st;
+  return pa_reduce(ws, need, context_lens, num_seqs, num_q_heads, pool->head_dim, max_context_len,
+                   partition_size, pool->dtype, out, stream);
 }
 
 }  // extern "C"

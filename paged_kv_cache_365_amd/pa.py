@@ -32,7 +32,9 @@ BLOCK_SIZE = 16
 EXPORTS = ("pa_init_pool", "pa_write_kv", "pa_decode_workspace_bytes", "pa_decode",
            "pa_verify_decode", "pa_decode_shared_prefix", "pa_write_kv_k8", "pa_decode_k8", "pa_write_kv_k2", "pa_decode_k2",
            "pa_reduce", "pa_debug_slot_ids", "pa_copy_blocks", "pa_gather_blocks",
-           "pa_scatter_blocks", "pa_probe_read", "pa_probe_read_tiles", "pa_status_string")
+           "pa_scatter_blocks", "pa_probe_read", "pa_probe_read_tiles", "pa_decode_split_static",
+           "pa_status_string")
+STATIC_SCRATCH_BYTES = 32 << 20   # PA_STATIC_SCRATCH_BYTES
 
 
 STATUS_NAMES = {PA_OK: "PA_OK", PA_ERR_INVALID_ARG: "PA_ERR_INVALID_ARG",
@@ -105,6 +107,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_gather_blocks.argtypes = [desc, vp, vp, vp, i32, vp, vp, vp]
     lib.pa_scatter_blocks.restype = ctypes.c_int
     lib.pa_scatter_blocks.argtypes = [desc, vp, vp, vp, i32, vp, vp, vp]
+    lib.pa_decode_split_static.restype = ctypes.c_int
+    lib.pa_decode_split_static.argtypes = [desc, vp, vp, vp, vp, i32, vp, i32, i32, i32,
+                                           ctypes.c_float, i32, vp, vp]
     lib.pa_probe_read.restype = ctypes.c_int
     lib.pa_probe_read.argtypes = [vp, sz, vp, i32, vp]
     lib.pa_probe_read_tiles.restype = ctypes.c_int
@@ -446,6 +451,22 @@ def pa_scatter_blocks(k_pool, v_pool, block_ids, k_src, v_src, stream=None) -> N
     _check("pa_scatter_blocks", load().pa_scatter_blocks(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), int(block_ids.shape[0]),
         _ptr(k_src), _ptr(v_src), _stream(stream)))
+
+
+def pa_decode_split_static(q, k_pool, v_pool, block_tables, context_lens, max_context_len: int,
+                           scale: float, partition_size: int, out, stream=None) -> None:
+    """pa_decode (split) + pa_reduce with the partials in the library's fixed
+    device array: no workspace, nothing allocated.  Calls overlapping on one GPU
+    race (one array per GPU)."""
+    chk = _Args("pa_decode_split_static")
+    desc = pool_desc(k_pool, v_pool, chk)
+    _decode_args(chk, desc, q, k_pool, v_pool, block_tables, context_lens, None, out, 3)
+    B, Hq, _ = q.shape
+    chk.on_gpu()
+    _check("pa_decode_split_static", load().pa_decode_split_static(
+        ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        int(block_tables.shape[1]), _ptr(context_lens), B, Hq, int(max_context_len),
+        float(scale), int(partition_size), _ptr(out), _stream(stream)))
 
 
 def pa_probe_read(src, sink, stream=None) -> None:

@@ -281,3 +281,24 @@ def test_read_probes_reject_bad_arguments(lib):
     bs8 = _desc(dtype=pa.PA_BF16, bs=8)
     assert t(ctypes.byref(bs8), FAKE, FAKE, FAKE, 8, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_UNSUPPORTED
     assert t(ctypes.byref(bf), FAKE + 8, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_MISALIGNED
+
+
+def test_static_scratch_entry_refuses_before_launching(lib):
+    """pa_decode_split_static: arguments and the fixed array's size are checked
+    before the device is touched (these calls return on a machine without a GPU)."""
+    f = lib.pa_decode_split_static
+    bf = _desc(dtype=pa.PA_BF16, d=128)
+    args = lambda **kw: [ctypes.byref(kw.get("desc", bf)), FAKE, FAKE, FAKE, FAKE,
+                         kw.get("mbs", 256), FAKE, kw.get("B", 2), kw.get("Hq", 8),
+                         kw.get("L", 40), ctypes.c_float(0.1), kw.get("P", 16),
+                         kw.get("out", FAKE), None]
+    need_huge = lib.pa_decode_workspace_bytes(4096, 64, 128, 4096, 16)
+    assert need_huge > pa.STATIC_SCRATCH_BYTES
+    assert f(*args(B=4096, Hq=64, L=4096)) == pa.PA_ERR_WORKSPACE
+    assert f(*args(P=0)) == pa.PA_ERR_INVALID_ARG          # split mode only
+    assert f(*args(P=24)) == pa.PA_ERR_INVALID_ARG         # multiple of 16
+    assert f(*args(out=None)) == pa.PA_ERR_INVALID_ARG
+    k8 = _desc(dtype=pa.PA_K8_BF16, d=128)
+    assert f(*args(desc=k8)) == pa.PA_ERR_UNSUPPORTED
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 8, 40, ctypes.c_float(0.1), 16, FAKE,
+             None) == pa.PA_ERR_INVALID_ARG
