@@ -2,7 +2,7 @@
 //
 // Element types are carried as raw bits; every 16-byte load brings VEC
 // elements to a lane and is widened to float32 here.  Block-table arithmetic
-// lives in exactly one place (pa_physical_block / pa_slot / pa_tile_offset) so
+// lives in exactly one place (pa_clamp_block / pa_slot / pa_tile_offset) so
 // that the debug slot-id kernel and the decode kernels compute the same
 // addresses.
 #pragma once
@@ -72,11 +72,23 @@ struct BF16 {
 // ---------------------------------------------------------------------------
 // Physical block of logical block `logical` of a table row, clamped into the
 // pool so that a corrupt table cannot address memory outside it.
-__device__ __forceinline__ int pa_physical_block(const int32_t* __restrict__ table_row,
-                                                 int logical, int num_blocks) {
-  int b = table_row[logical];
+__device__ __forceinline__ int pa_clamp_block(int b, int num_blocks) {
   b = b < 0 ? 0 : b;
   return b >= num_blocks ? num_blocks - 1 : b;
+}
+__device__ __forceinline__ int pa_physical_block(const int32_t* __restrict__ table_row,
+                                                 int logical, int num_blocks) {
+  return pa_clamp_block(table_row[logical], num_blocks);
+}
+// The same for a wave-uniform logical index, read through the scalar cache
+// (the constant address space: tables are never written while a kernel runs),
+// so that waiting for the id counts scalar loads only and leaves the vector
+// loads of K/V tiles in flight.
+__device__ __forceinline__ int pa_physical_block_uniform(const int32_t* __restrict__ table_row,
+                                                         int logical, int num_blocks) {
+  typedef const __attribute__((address_space(4))) int32_t ScalarI32;
+  return pa_clamp_block(((ScalarI32*)table_row)[__builtin_amdgcn_readfirstlane(logical)],
+                        num_blocks);
 }
 
 // Slot of token t held by physical block `physical` of a pool of bs-token blocks.

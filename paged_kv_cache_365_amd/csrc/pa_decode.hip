@@ -43,6 +43,12 @@
 //           B = P: lane l already holds the weights of tokens 4q .. 4q+3 for
 //               row r -- the logits' own output layout -- so P never moves.
 //           out: lane l holds O[row r][16 cb + 4q .. 16 cb + 4q + 3].
+//   The LDS-ring workgroups (kLds) take two steps per pass: both steps'
+//   logits, one softmax update for their 32 tokens, and P.V as one
+//   16 x 16 x 32 product per 16 columns, whose contraction index runs over
+//   the lane's 4 tokens of the first step and then of the second (pv2) -- half
+//   the matrix-core instructions of two 16 x 16 x 16 products, and half the
+//   barriers and softmax reductions.
 //
 // Int8 keys (MmaK8) feed the same logits product with f16 operands: the codes
 // convert exactly and the per-channel scales ride on the query (see MmaK8).
@@ -160,6 +166,21 @@ struct MmaBF16 {
     v.x &= static_cast<uint32_t>(bits);
     v.y &= static_cast<uint32_t>(bits >> 32);
   }
+  // Two steps in one 32-deep product: lane (r, q) holds V tokens 4q .. 4q+3 of
+  // step a then of step b (column 16 cb + r; v = {a, b}) and the same 8
+  // tokens' weights of row r -- the contraction index k = 8q + e runs over
+  // both steps.
+  static __device__ __forceinline__ f32x4 pv2(const uint4& v, const uint4& p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v),
+                                                   __builtin_bit_cast(bf16x8, p), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint4 pack8(const float (&p)[8], float& sum) {
+    const float a[4] = {p[0], p[1], p[2], p[3]};
+    const float b[4] = {p[4], p[5], p[6], p[7]};
+    const POp pa = pack(a, sum);
+    const POp pb = pack(b, sum);
+    return make_uint4(pa.x, pa.y, pb.x, pb.y);
+  }
 };
 
 struct MmaF16 {
@@ -186,6 +207,17 @@ struct MmaF16 {
     return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
   }
   static __device__ __forceinline__ void keep(VLoad& v, int n) { MmaBF16::keep(v, n); }
+  static __device__ __forceinline__ f32x4 pv2(const uint4& v, const uint4& p, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, v),
+                                                  __builtin_bit_cast(f16x8, p), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint4 pack8(const float (&p)[8], float& sum) {
+    const float a[4] = {p[0], p[1], p[2], p[3]};
+    const float b[4] = {p[4], p[5], p[6], p[7]};
+    const POp pa = pack(a, sum);
+    const POp pb = pack(b, sum);
+    return make_uint4(pa.x, pa.y, pb.x, pb.y);
+  }
 };
 
 struct MmaF32 {
@@ -347,15 +379,17 @@ struct Phys {
 // registers per lane and SIMD): the ring of kDepth steps, the accumulators and
 // the query operands of a lane fit 168 registers at d 128 with one chunk (three
 // waves), 256 with two; float32 tiles are twice as large.
-template <class M, int D, int kChunks>
+template <class M, int D, int kChunks, bool kLds>
 constexpr int min_waves_per_simd() {
   if constexpr (M::kKBytes == 4) return D == 128 ? 2 : (kChunks == 1 ? 3 : 2);
+  // the LDS ring reads two tiles per pass into registers
+  if constexpr (kLds) return D == 128 ? 3 : 4;
   return D == 128 ? (kChunks == 1 ? 3 : 2) : (kChunks == 1 ? 5 : 3);
 }
 
 template <class M, class Tr, int D, int kWaves, int kChunks, bool kShared, int kBS,
           bool kWavePart, bool kLds = false, bool kPrefix = false>
-__global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>())) void decode_kernel(
+__global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLds>())) void decode_kernel(
     DecodeArgs a) {
   // kLds: four waves hold the four 16-row chunks of 64 rows and share each
   // step's tile through an LDS ring (see below); otherwise every wave holds all
@@ -560,12 +594,15 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   // when the context ends inside the first: its tokens are masked anyway).
   const int live_blocks = (L + kBS - 1) / kBS;
   auto physical = [&](int jb) {
+    // every caller's step index is wave-uniform: the ids come through the
+    // scalar cache, and waiting for them leaves the tile loads in flight
     Phys p;
     if constexpr (kBS == 16) {
-      p.a = p.b = pa_physical_block(trow, jb, a.num_blocks);
+      p.a = p.b = pa_physical_block_uniform(trow, jb, a.num_blocks);
     } else {
-      p.a = pa_physical_block(trow, 2 * jb, a.num_blocks);
-      p.b = 2 * jb + 1 < live_blocks ? pa_physical_block(trow, 2 * jb + 1, a.num_blocks) : p.a;
+      p.a = pa_physical_block_uniform(trow, 2 * jb, a.num_blocks);
+      p.b = 2 * jb + 1 < live_blocks ? pa_physical_block_uniform(trow, 2 * jb + 1, a.num_blocks)
+                                     : p.a;
     }
     return p;
   };
@@ -668,17 +705,20 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
   auto step_of = [&](int i) { return first + i * kStride; };
   if constexpr (kLds) {
     // The four waves hold the four 16-row chunks of the workgroup's 64 rows
-    // and walk the same steps.  Each step's tile is read from memory once:
-    // wave w loads K operands w, w + 4, ... and V operands w, w + 4, ... (for
-    // every lane), writes them to a two-slot LDS ring, and after one barrier
-    // every wave reads the whole tile back as its own operands.
+    // and walk the same steps, two at a time.  Each step's tile is read from
+    // memory once: wave w loads K operands w, w + 4, ... and V operands w,
+    // w + 4, ... (for every lane) of both steps of a pair, writes them to a
+    // two-pair LDS ring, and after one barrier every wave reads both tiles back
+    // as its own operands.
     constexpr int kKS = (kKLoads + 3) / 4;
     constexpr int kVS = (kColBlocks + 3) / 4;
-    constexpr int kAhead = 2;  // steps staged in registers ahead of the LDS ring
-    __shared__ uint4 lds_k[2][kKLoads][64];
-    __shared__ VLoad lds_v[2][kColBlocks][64];
-    uint4 sk[kAhead][kKS];
-    VLoad sv[kAhead][kVS];
+    // K: [pair slot * 2 + step][operand][lane]; V: [pair slot][operand][lane]
+    // holding the lane's operand of step a in its low and of step b in its high
+    // 8 bytes, so one read returns the 32-deep P.V operand
+    __shared__ uint4 lds_k[4][kKLoads][64];
+    __shared__ uint4 lds_v[2][kColBlocks][64];
+    uint4 sk[2][kKS];
+    VLoad sv[2][kVS];
     auto stage = [&](Phys ph, uint4 (&k)[kKS], VLoad (&v)[kVS]) {
       const TilePtrs p = tile_ptrs(ph);
 #pragma unroll
@@ -687,51 +727,120 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks>()))
       for (int i = 0; i < kVS; ++i)
         v[i] = load16<kStreamV>(v_at(p, min(wave + 4 * i, kColBlocks - 1)));
     };
+    // Steps ja and ja + 1 in one pass: their logits, one raise decision and one
+    // set of rounded weights for the 32 tokens, and P.V as one 16x16x32 product
+    // per 16 columns (pv2).  A step past the partition is entirely masked.
+    auto consume_pair = [&](int ja, const uint4 (&ka)[kKLoads], const uint4 (&kb)[kKLoads],
+                            uint4 (&vv)[kColBlocks]) {
+      const int tok_a = ja * kStep + 4 * qg;  // first token of this lane's four in step ja
+      const int tok_b = tok_a + kStep;
+      if ((ja + 2) * kStep > t_hi) {  // V rows past the partition (wave-uniform test)
+        const int na = min(max(t_hi - tok_a, 0), 4);
+        const int nb = min(max(t_hi - tok_b, 0), 4);
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb) {
+          VLoad va = make_uint2(vv[cb].x, vv[cb].y);
+          VLoad vb = make_uint2(vv[cb].z, vv[cb].w);
+          M::keep(va, na);
+          M::keep(vb, nb);
+          vv[cb] = make_uint4(va.x, va.y, vb.x, vb.y);
+        }
+      }
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kKLoads; ++j) {
+        sa = M::qk(ka[j], &qop[0][j * M::kQOps], sa);
+        sb = M::qk(kb[j], &qop[0][j * M::kQOps], sb);
+      }
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = sa[i] * qs[0];
+        x[4 + i] = sb[i] * qs[0];
+      }
+      if ((ja + 2) * kStep > t_hi_min) {  // wave-uniform
+        const int na = min(max(row_hi[0] - tok_a, 0), 4);
+        const int nb = min(max(row_hi[0] - tok_b, 0), 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i >= na) x[i] = -INFINITY;
+          if (i >= nb) x[4 + i] = -INFINITY;
+        }
+      }
+      const float bmax = max_over_q(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
+      const bool raise = bmax > m[0] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {  // wave-uniform
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m[0] - bmax) : 1.f;  // 0 on a first step
+        m[0] = raise ? bmax : m[0];
+        lsum[0] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb) acc[0][cb] *= alpha;
+      }
+      const float mref = m[0] == -INFINITY ? 0.f : m[0];  // a row that has seen no token yet
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+      const uint4 pop = M::pack8(p, lsum[0]);
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) acc[0][cb] = M::pv2(vv[cb], pop, acc[0][cb]);
+    };
     const int nl = blk_hi - blk_lo;  // workgroup-uniform: every wave walks every step
     if (nl > 0) {
       // in step order (the waits below count on step d's loads being older
       // than step d + 1's)
-#pragma unroll
-      for (int d = 0; d < kAhead; ++d) {
-        stage(physical(blk_lo + min(d, nl - 1)), sk[d], sv[d]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      Phys next = physical(blk_lo + min(kAhead, nl - 1));
-      // one step: publish its staged tile share, stage the step kAhead ahead
-      // (the last one again past the end: no branch, so the waits before the
-      // ring writes stay exact), barrier, read the whole tile back, compute
-      auto lds_step = [&](int i, uint4 (&k)[kKS], VLoad (&v)[kVS], int slot) {
+      stage(physical(blk_lo), sk[0], sv[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      stage(physical(blk_lo + min(1, nl - 1)), sk[1], sv[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      Phys next_a = physical(blk_lo + min(2, nl - 1));
+      Phys next_b = physical(blk_lo + min(3, nl - 1));
+      // pair i (steps 2i, 2i + 1) in ring slot `slot`: publish its staged tile
+      // shares, stage pair i + 1 (the last step again past the end: no branch,
+      // so the waits before the ring writes stay exact), barrier, read both
+      // tiles back, compute
+      auto lds_pair = [&](int i, int slot) {
         // (with fewer than four operands of a kind, two waves load and write
-        // the same one: equal values, so the duplicate write is harmless)
+        // the same one: equal values, so the duplicate write is harmless).
+        // Each half is written and then re-staged before the other half is
+        // written, so the wait before a write covers that step's loads only and
+        // the other step's loads stay in flight: the load queue never drains.
 #pragma unroll
-        for (int t = 0; t < kKS; ++t) lds_k[slot][min(wave + 4 * t, kKLoads - 1)][lane] = k[t];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int t = 0; t < kVS; ++t) lds_v[slot][min(wave + 4 * t, kColBlocks - 1)][lane] = v[t];
-        stage(next, k, v);
-        next = physical(blk_lo + min(i + kAhead + 1, nl - 1));
-        __syncthreads();
-        uint4 kr[kKLoads];
-        VLoad vr[kColBlocks];
+          for (int t = 0; t < kKS; ++t)
+            lds_k[2 * slot + h][min(wave + 4 * t, kKLoads - 1)][lane] = sk[h][t];
 #pragma unroll
-        for (int j = 0; j < kKLoads; ++j) kr[j] = lds_k[slot][j][lane];
-#pragma unroll
-        for (int cb = 0; cb < kColBlocks; ++cb) vr[cb] = lds_v[slot][cb][lane];
-        if (row0 < rows) consume(blk_lo + i, kr, vr);
-      };
-      int base = 0;
-      for (; base + kAhead <= nl; base += kAhead) {
-#pragma unroll
-        for (int u = 0; u < kAhead; ++u) lds_step(base + u, sk[u], sv[u], u & 1);
-      }
-      const int rem = nl - base;  // workgroup-uniform, < kAhead; one branch per count
-#pragma unroll
-      for (int R = 1; R < kAhead; ++R) {
-        if (rem == R) {
-#pragma unroll
-          for (int u = 0; u < R; ++u) lds_step(base + u, sk[u], sv[u], u & 1);
+          for (int t = 0; t < kVS; ++t)
+            reinterpret_cast<VLoad*>(&lds_v[slot][min(wave + 4 * t, kColBlocks - 1)][lane])[h] =
+                sv[h][t];
+          stage(h == 0 ? next_a : next_b, sk[h], sv[h]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        next_a = physical(blk_lo + min(2 * i + 4, nl - 1));
+        next_b = physical(blk_lo + min(2 * i + 5, nl - 1));
+        __syncthreads();
+        uint4 ka[kKLoads], kb[kKLoads], vv[kColBlocks];
+#pragma unroll
+        for (int j = 0; j < kKLoads; ++j) {
+          ka[j] = lds_k[2 * slot][j][lane];
+          kb[j] = lds_k[2 * slot + 1][j][lane];
+        }
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb) vv[cb] = lds_v[slot][cb][lane];
+        if (row0 < rows) consume_pair(blk_lo + 2 * i, ka, kb, vv);
+      };
+      const int np = (nl + 1) / 2;  // workgroup-uniform
+      int i = 0;
+      for (; i + 2 <= np; i += 2) {
+        lds_pair(i, 0);
+        lds_pair(i + 1, 1);
       }
+      if (i < np) lds_pair(i, 0);  // pairs alternate slots: an even index takes slot 0
     }
+    // every lane of a row holds the row's whole sum: one share, for the
+    // four-lane sum below
   }
   if (!kLds && n > 0) {  // wave-uniform
     // prologue: steps 0 .. kDepth-2 (an index past the last step reloads it)
@@ -1025,8 +1134,15 @@ hipError_t launch_prefix_c(DecodeArgs a, hipStream_t stream) {
 template <class M, class Tr, int D>
 hipError_t launch_prefix_t(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  // float32 tiles at d 128 fill the registers with one chunk already
-  const bool two = group > 16 && !(M::kKBytes == 4 && D == 128);
+  // Two row chunks per workgroup as soon as the prefix role has more than 32
+  // rows (every sequence's rows of a KV head): half the sibling workgroups,
+  // each prefix tile read half as often from the XCD's L2 (shared-prefix batch,
+  // 128 sequences x 4 rows, 1024-token partitions: 59.2 -> 56.5 us per step;
+  // at 512-token partitions, one wave per partition, one chunk stays ahead:
+  // 60.3 vs 63.5).  Float32 tiles at d 128 fill the registers with one chunk.
+  const bool two = (group > 16 || (static_cast<int64_t>(a.num_seqs) * group > 32 &&
+                                   a.partition_tokens > kPrefixWavePartTokens)) &&
+                   !(M::kKBytes == 4 && D == 128);
   if (a.block_size == 8)
     return two ? launch_prefix_c<M, Tr, D, 2, 8>(a, stream) : launch_prefix_c<M, Tr, D, 1, 8>(a, stream);
   return two ? launch_prefix_c<M, Tr, D, 2, 16>(a, stream) : launch_prefix_c<M, Tr, D, 1, 16>(a, stream);
