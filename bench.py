@@ -34,13 +34,18 @@ DECODE_SOURCES = ("pa_decode.hip", "pa_common.h", "pa_internal.h", "pa_units.h")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the decode kernel is compiled from, to tell whether
-    stored counters still apply."""
+    """Hash of the code the decode kernel is compiled from (comments and blank
+    lines left out), to tell whether stored counters still apply."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_365_amd", "csrc")
     for name in DECODE_SOURCES:
+        text = open(os.path.join(csrc, name), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
         h.update(name.encode())
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

@@ -714,7 +714,10 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
     constexpr int kVS = (kColBlocks + 3) / 4;
     // K: [pair slot * 2 + step][operand][lane]; V: [pair slot][operand][lane]
     // holding the lane's operand of step a in its low and of step b in its high
-    // 8 bytes, so one read returns the 32-deep P.V operand
+    // 8 bytes, so one 16-byte read returns the 32-deep P.V operand.  (The
+    // 8-byte stores at a 16-byte lane stride conflict on LDS banks; keeping the
+    // two halves as separate 512-byte runs removes the conflicts but measured
+    // slower: 8-token draft ~201/211 -> ~217/223 us.)
     __shared__ uint4 lds_k[4][kKLoads][64];
     __shared__ uint4 lds_v[2][kColBlocks][64];
     uint4 sk[2][kKS];

@@ -72,7 +72,12 @@ def test_kernel_source_hash_follows_the_sources(tmp_path, monkeypatch):
         (csrc / name).write_bytes(open(src, "rb").read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.kernel_source_hash() == h
-    (csrc / "pa_common.h").write_bytes((csrc / "pa_common.h").read_bytes() + b"\n")
+    # a comment or a blank line leaves the code, and the hash, as they were
+    (csrc / "pa_common.h").write_bytes((csrc / "pa_common.h").read_bytes() + b"\n// note\n\n")
+    assert bench.kernel_source_hash() == h
+    # a change to the code does not
+    (csrc / "pa_common.h").write_bytes((csrc / "pa_common.h").read_bytes() +
+                                       b"\nnamespace pa { constexpr int kUnused = 1; }\n")
     assert bench.kernel_source_hash() != h
 
 
