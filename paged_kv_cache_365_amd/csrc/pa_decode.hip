@@ -714,18 +714,17 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
     constexpr int kVS = (kColBlocks + 3) / 4;
     // K: [pair slot * 2 + step][operand][lane]; V: [pair slot][operand][lane]
     // holding the lane's operand of step a in its low and of step b in its high
-    // 8 bytes, so one 16-byte read returns the 32-deep P.V operand.  (The
-    // 8-byte stores at a 16-byte lane stride conflict on LDS banks; keeping the
-    // two halves as separate 512-byte runs removes the conflicts but measured
-    // slower: 8-token draft ~201/211 -> ~217/223 us.)
+    // 8 bytes, so one 16-byte read returns the 32-deep P.V operand, and one
+    // 16-byte store per lane writes both steps' shares.
     __shared__ uint4 lds_k[4][kKLoads][64];
     __shared__ uint4 lds_v[2][kColBlocks][64];
     uint4 sk[2][kKS];
     VLoad sv[2][kVS];
-    auto stage = [&](Phys ph, uint4 (&k)[kKS], VLoad (&v)[kVS]) {
-      const TilePtrs p = tile_ptrs(ph);
+    auto stage_k = [&](const TilePtrs& p, uint4 (&k)[kKS]) {
 #pragma unroll
       for (int i = 0; i < kKS; ++i) k[i] = load16<kStreamK>(k_at(p, min(wave + 4 * i, kKLoads - 1)));
+    };
+    auto stage_v = [&](const TilePtrs& p, VLoad (&v)[kVS]) {
 #pragma unroll
       for (int i = 0; i < kVS; ++i)
         v[i] = load16<kStreamV>(v_at(p, min(wave + 4 * i, kColBlocks - 1)));
@@ -791,36 +790,48 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
     };
     const int nl = blk_hi - blk_lo;  // workgroup-uniform: every wave walks every step
     if (nl > 0) {
-      // in step order (the waits below count on step d's loads being older
-      // than step d + 1's)
-      stage(physical(blk_lo), sk[0], sv[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      stage(physical(blk_lo + min(1, nl - 1)), sk[1], sv[1]);
-      __builtin_amdgcn_sched_barrier(0);
+      // the first pair, in the order every pass issues its loads (the waits
+      // below count on it): K of step a, K of step b, V of both
+      {
+        const TilePtrs pa = tile_ptrs(physical(blk_lo));
+        const TilePtrs pb = tile_ptrs(physical(blk_lo + min(1, nl - 1)));
+        stage_k(pa, sk[0]);
+        stage_k(pb, sk[1]);
+        stage_v(pa, sv[0]);
+        stage_v(pb, sv[1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       Phys next_a = physical(blk_lo + min(2, nl - 1));
       Phys next_b = physical(blk_lo + min(3, nl - 1));
       // pair i (steps 2i, 2i + 1) in ring slot `slot`: publish its staged tile
       // shares, stage pair i + 1 (the last step again past the end: no branch,
       // so the waits before the ring writes stay exact), barrier, read both
-      // tiles back, compute
+      // tiles back, compute.  The loads of a pair are issued in the order K of
+      // step a, K of step b, V of both: each K share is written and re-staged
+      // before the next wait, and the two steps' V shares go out as one 16-byte
+      // store per operand, so at every wait the next loads are already in
+      // flight and no LDS store is narrower than 16 bytes (8-byte stores at a
+      // 16-byte stride conflict on the banks).  With fewer than four operands of
+      // a kind, two waves load and write the same one: equal values, so the
+      // duplicate write is harmless.
       auto lds_pair = [&](int i, int slot) {
-        // (with fewer than four operands of a kind, two waves load and write
-        // the same one: equal values, so the duplicate write is harmless).
-        // Each half is written and then re-staged before the other half is
-        // written, so the wait before a write covers that step's loads only and
-        // the other step's loads stay in flight: the load queue never drains.
+        const TilePtrs pa = tile_ptrs(next_a);
+        const TilePtrs pb = tile_ptrs(next_b);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int t = 0; t < kKS; ++t) lds_k[2 * slot][min(wave + 4 * t, kKLoads - 1)][lane] = sk[0][t];
+        stage_k(pa, sk[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < kKS; ++t)
-            lds_k[2 * slot + h][min(wave + 4 * t, kKLoads - 1)][lane] = sk[h][t];
+        for (int t = 0; t < kKS; ++t) lds_k[2 * slot + 1][min(wave + 4 * t, kKLoads - 1)][lane] = sk[1][t];
+        stage_k(pb, sk[1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < kVS; ++t)
-            reinterpret_cast<VLoad*>(&lds_v[slot][min(wave + 4 * t, kColBlocks - 1)][lane])[h] =
-                sv[h][t];
-          stage(h == 0 ? next_a : next_b, sk[h], sv[h]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int t = 0; t < kVS; ++t)
+          lds_v[slot][min(wave + 4 * t, kColBlocks - 1)][lane] =
+              make_uint4(sv[0][t].x, sv[0][t].y, sv[1][t].x, sv[1][t].y);
+        stage_v(pa, sv[0]);
+        stage_v(pb, sv[1]);
+        __builtin_amdgcn_sched_barrier(0);
         next_a = physical(blk_lo + min(2 * i + 4, nl - 1));
         next_b = physical(blk_lo + min(2 * i + 5, nl - 1));
         __syncthreads();
