@@ -367,13 +367,16 @@ pa_status pa_decode_split_static(const pa_pool_desc* pool, const void* q, const 
  *   workgroup of 8 wavefronts per (sequence, KV head), wavefront w reads the
  *   16-token blocks w, w + 8, ... through the block table.  16-bit pools of
  *   16-token blocks, head_dim 64 or 128; physical ids and lengths are clamped
- *   as in pa_decode.  sink holds num_seqs * num_kv_heads * 8 words. */
+ *   as in pa_decode.  sink holds sink_words 32-bit words, at least
+ *   num_seqs * num_kv_heads * 8 (one per wavefront); fewer is
+ *   PA_ERR_INVALID_ARG. */
 pa_status pa_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t sink_words,
                         hipStream_t stream);
 pa_status pa_probe_read_tiles(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t num_seqs,
-                              int32_t max_context_len, uint32_t* sink, hipStream_t stream);
+                              int32_t max_context_len, uint32_t* sink, int32_t sink_words,
+                              hipStream_t stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char* pa_status_string(pa_status status);

@@ -113,7 +113,8 @@ pa_status pa_probe_read(const void* src, size_t bytes, uint32_t* sink, int32_t s
 pa_status pa_probe_read_tiles(const pa_pool_desc* pool, const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, int32_t max_blocks_per_seq,
                               const int32_t* context_lens, int32_t num_seqs,
-                              int32_t max_context_len, uint32_t* sink, hipStream_t stream) {
+                              int32_t max_context_len, uint32_t* sink, int32_t sink_words,
+                              hipStream_t stream) {
   if (!pool || !k_pool || !v_pool || !block_tables || !context_lens || !sink)
     return PA_ERR_INVALID_ARG;
   if (num_seqs <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || pool->num_blocks <= 0 ||
@@ -125,6 +126,8 @@ pa_status pa_probe_read_tiles(const pa_pool_desc* pool, const void* k_pool, cons
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * 16)
     return PA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(num_seqs) * pool->num_kv_heads > INT32_MAX / 8) return PA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(sink_words) < static_cast<int64_t>(num_seqs) * pool->num_kv_heads * 8)
+    return PA_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(k_pool) % 16 != 0 || reinterpret_cast<uintptr_t>(v_pool) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(block_tables) % 4 != 0 ||
       reinterpret_cast<uintptr_t>(context_lens) % 4 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)

@@ -113,7 +113,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.pa_probe_read.restype = ctypes.c_int
     lib.pa_probe_read.argtypes = [vp, sz, vp, i32, vp]
     lib.pa_probe_read_tiles.restype = ctypes.c_int
-    lib.pa_probe_read_tiles.argtypes = [desc, vp, vp, vp, i32, vp, i32, i32, vp, vp]
+    lib.pa_probe_read_tiles.argtypes = [desc, vp, vp, vp, i32, vp, i32, i32, vp, i32, vp]
     if path is None:
         _lib = lib
     return lib
@@ -494,7 +494,7 @@ def pa_probe_read_tiles(k_pool, v_pool, block_tables, context_lens, max_context_
     _check("pa_probe_read_tiles", load().pa_probe_read_tiles(
         ctypes.byref(desc), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
         int(block_tables.shape[1]), _ptr(context_lens), B, int(max_context_len), _ptr(sink),
-        _stream(stream)))
+        int(sink.numel()), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -273,14 +273,16 @@ def test_read_probes_reject_bad_arguments(lib):
     assert p(FAKE + 8, 1024, FAKE, 8, None) == pa.PA_ERR_MISALIGNED
     t = lib.pa_probe_read_tiles
     bf = _desc(dtype=pa.PA_BF16, d=128)
-    assert t(None, FAKE, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_INVALID_ARG
-    assert t(ctypes.byref(bf), FAKE, FAKE, FAKE, 4, FAKE, 0, 40, FAKE, None) == pa.PA_ERR_INVALID_ARG
-    assert t(ctypes.byref(bf), FAKE, FAKE, FAKE, 2, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_INVALID_ARG
+    assert t(None, FAKE, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, 64, None) == pa.PA_ERR_INVALID_ARG
+    assert t(ctypes.byref(bf), FAKE, FAKE, FAKE, 4, FAKE, 0, 40, FAKE, 64, None) == pa.PA_ERR_INVALID_ARG
+    assert t(ctypes.byref(bf), FAKE, FAKE, FAKE, 2, FAKE, 2, 40, FAKE, 64, None) == pa.PA_ERR_INVALID_ARG
     f32 = _desc(dtype=pa.PA_F32)
-    assert t(ctypes.byref(f32), FAKE, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_UNSUPPORTED
+    assert t(ctypes.byref(f32), FAKE, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, 64, None) == pa.PA_ERR_UNSUPPORTED
     bs8 = _desc(dtype=pa.PA_BF16, bs=8)
-    assert t(ctypes.byref(bs8), FAKE, FAKE, FAKE, 8, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_UNSUPPORTED
-    assert t(ctypes.byref(bf), FAKE + 8, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, None) == pa.PA_ERR_MISALIGNED
+    assert t(ctypes.byref(bs8), FAKE, FAKE, FAKE, 8, FAKE, 2, 40, FAKE, 64, None) == pa.PA_ERR_UNSUPPORTED
+    assert t(ctypes.byref(bf), FAKE + 8, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, 64, None) == pa.PA_ERR_MISALIGNED
+    # one sink word per wavefront: 2 sequences x 2 KV heads x 8 wavefronts
+    assert t(ctypes.byref(bf), FAKE, FAKE, FAKE, 4, FAKE, 2, 40, FAKE, 31, None) == pa.PA_ERR_INVALID_ARG
 
 
 def test_static_scratch_entry_refuses_before_launching(lib):
