@@ -156,8 +156,12 @@ struct MmaBF16 {
     const bf16x2 b = {static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
     const uint32_t ua = __builtin_bit_cast(uint32_t, a);
     const uint32_t ub = __builtin_bit_cast(uint32_t, b);
-    sum += (__uint_as_float(ua << 16) + __uint_as_float(ua & 0xffff0000u)) +
-           (__uint_as_float(ub << 16) + __uint_as_float(ub & 0xffff0000u));
+    // the running sum takes both rounded weights of a pair in one dot product
+    // with (1, 1): the products are exact, and one instruction replaces the
+    // widening and adding of each half
+    const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    sum = __builtin_amdgcn_fdot2_f32_bf16(a, one, sum, false);
+    sum = __builtin_amdgcn_fdot2_f32_bf16(b, one, sum, false);
     return make_uint2(ua, ub);
   }
   // keep the first n (0..4) tokens of a V load, zero the rest
