@@ -312,12 +312,15 @@ struct MmaK8 {
 // out) of the 16-bit type of VM.  One load per tile: lane (r, q) reads the
 // D / 64 words of token r and channel group q (8 bytes at d 128, 4 at d 64),
 // which hold channels 32 j + 8 q + e (e = 0..7) for all D / 32 logit steps j:
-// step j is word j / 2, half j % 2, and ((word >> 2 (4 h + i)) & 0x30003) is
-// the pair of codes e = 2i, 2i + 1 in the low bits of two 16-bit halves.  Or-ing
-// in 0x6400 makes each half the f16 1024 + code; subtracting 1024 leaves the
-// code exactly.  The B operand is q' = q * step per channel (times a power of
-// two per row, as for int8 keys), and the zero points add the same
-// scale * sum_c q_c z_c to every logit of a row (kept in qb).
+// step j is word j / 2, half j % 2 (bits 8 and up of the word, shifted down
+// by 8, for half 1), and (word & (0x30003 << 2i)) keeps the codes of the pair
+// e = 2i, 2i + 1 in place, at bits 2i and 16 + 2i.  Or-ing in 0x6400 makes each
+// half the f16 1024 + code * 4^i (at most 1216: exact), and subtracting 1024
+// leaves code * 4^i exactly -- no shift per pair.  The B operand is
+// q' = q * step per channel (times a power of two per row, as for int8 keys)
+// times 4^-i for the elements of pair i, so the products are unchanged; the
+// zero points add the same scale * sum_c q_c z_c to every logit of a row
+// (kept in qb).
 template <class VM, int D>
 struct MmaK2 {
   static constexpr int kKBytes = 0;  // sub-byte keys
@@ -335,9 +338,10 @@ struct MmaK2 {
     }
   }
   static __device__ __forceinline__ f16x8 codes(uint32_t w, int h) {
+    const uint32_t x = h ? (w >> 8) : w;
     u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ((w >> (2 * (4 * h + i))) & 0x00030003u) | 0x64006400u;
+    for (int i = 0; i < 4; ++i) v[i] = (x & (0x00030003u << (2 * i))) | 0x64006400u;
     return __builtin_bit_cast(f16x8, v) - static_cast<_Float16>(1024.0f);
   }
   static __device__ __forceinline__ f32x4 qk(const KLoad& k, const uint4* q, f32x4 c) {
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
       for (int j = 0; j < kQOps; ++j) {
         f16x8 h;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) h[t] = static_cast<_Float16>(qp[j][t] * up);
+        for (int t = 0; t < 8; ++t) h[t] = static_cast<_Float16>(qp[j][t] * up * ldexpf(1.f, -2 * (t >> 1)));
         const uint4 v = __builtin_bit_cast(uint4, h);
         qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
       }
