@@ -428,6 +428,12 @@ def main() -> int:
             "duration_source": duration_source,
         },
     }
+    if workload.startswith("70b"):
+        # one call is one attention layer; LLaMA-2 70B has 80 of them (the KV
+        # Cache section of "LLM推理优化实战：从KV Cache到Speculative Decoding，
+        # 把延迟打下来" sizes its cache with that count), so this is the
+        # attention-only decode rate of the whole model
+        rec["attention_tokens_per_s_80_layers"] = round(B * T / (80 * ms_per_step * 1e-3), 1)
     if w.prefix_blocks:
         # shared blocks counted once: the bytes a step must take from memory
         rec["unique_bytes_per_step"] = w.algorithmic_bytes(unique=True, query_tokens=T)
