@@ -50,6 +50,17 @@ def logit_gates(dtype: str, xmax: float, vmax: float) -> dict:
     return {"abs_tol": ABS_TOL[dtype] + 2.0 * vmax * e, "unit": UNIT[dtype] + e}
 
 
+def quantised_gates(dtype: str, qmag: float, vmax: float) -> dict:
+    """Gates for quantised keys: the B operand of their logit products is
+    q' = q * s rounded to f16 (relative error <= 2^-11 per element, whatever
+    the value type), so a logit is off by at most
+    e = 2^-11 * scale * sum_c |q_c s_c code_c| (qmag = the largest such sum
+    over the call, natural units); each weight then moves by about e
+    relatively, the output by at most 2 vmax e."""
+    e = 2.0 ** -11 * qmag
+    return {"abs_tol": ABS_TOL[dtype] + 2.0 * vmax * e, "unit": UNIT[dtype] + e}
+
+
 def scaled_bound(want: np.ndarray, dtype: str, unit: float | None = None) -> np.ndarray:
     """Per-element bound of the same shape as ``want`` (rows = last axis)."""
     want = np.asarray(want, dtype=np.float64)

@@ -1,8 +1,10 @@
 """A broad random parity sweep: every attention entry point of the C ABI
 (pa_decode, pa_verify_decode, pa_decode_k8, pa_decode_k2,
 pa_decode_shared_prefix, each followed by pa_reduce when split) on shapes drawn
-from the seed, against the fp64 oracle (tolerances of
-``tests/test_gpu_parity.py``).
+from the seed, against the fp64 oracle: the max-abs tolerances of
+``tests/test_gpu_parity.py`` and the scaled bound of ``tests/parity_bounds.py``
+on every element -- for int8 and 2-bit keys widened by the rounding of their
+f16 query operand q * s (``quantised_gates``).
 
 Each seed draws: the entry point (cycled), the value type (float32 / f16 / bf16;
 f16 / bf16 for quantised keys), head_dim 64 or 128, 1-8 KV heads, 1-64 query
@@ -21,6 +23,7 @@ from oracle import quantized_kv as qk
 from paged_kv_cache_365_amd import pa
 from paged_kv_cache_365_amd import workloads as wl
 from paged_kv_cache_365_amd.device import to_torch, upload, widen_f32
+from parity_bounds import assert_parity, quantised_gates
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -60,7 +63,26 @@ def draw(seed):
     return rng, kind, dtype, d, hkv, hkv * g, T, bs, P, prefix, lens
 
 
-@pytest.mark.parametrize("seed", range(150))
+def quantised_logit_mag(kind, q, w, keys, scales, dtype):
+    """The largest scale * sum_c |q_c s_c code_c| of the call (natural units):
+    the size of the f16-rounded products a quantised key's logit is made of."""
+    B, T, Hq, d = q.shape
+    G = Hq // w.num_kv_heads
+    sc32 = abs(float(np.float32(w.scale)))
+    mag = 0.0
+    for s in range(B):
+        L = int(w.context_lens[s])
+        for g in range(w.num_kv_heads):
+            if kind == "k8":
+                ke = np.abs(qk.dequantize_k(oracle.k_rows(keys, w.block_tables[s], L, g), scales[g]))
+            else:
+                ke = qk.k2_rows(keys, w.block_tables[s], L, g).astype(np.float64) * np.abs(scales[g])
+            qq = np.abs(oracle.widen(q[s, :, g * G:(g + 1) * G], dtype).reshape(-1, d))
+            mag = max(mag, float((qq @ ke.T).max(initial=0.0)) * sc32)
+    return mag
+
+
+@pytest.mark.parametrize("seed", range(1000))
 def test_random_sweep(seed):
     rng, kind, dtype, d, hkv, hq, T, bs, P, prefix, lens = draw(seed)
     case = (kind, dtype, d, hkv, hq, T, bs, P, prefix, lens)
@@ -105,3 +127,10 @@ def test_random_sweep(seed):
     assert np.isfinite(got).all(), case
     err = np.abs(got - want).max()
     assert err <= TOL[dtype], f"{case}: max-abs {err:.3e}"
+    gates = {}
+    if kind in ("k8", "k2"):
+        keys, scales = (codes, sc) if kind == "k8" else (words, st)
+        v = oracle.widen(w.v_pool, dtype)
+        vmax = float(np.abs(v[np.isfinite(v)]).max(initial=0.0))
+        gates = quantised_gates(dtype, quantised_logit_mag(kind, q, w, keys, scales, dtype), vmax)
+    assert_parity(got, want, dtype, f"sweep seed {seed} {kind}", **gates)

@@ -169,3 +169,82 @@ def test_bound_catches_a_dropped_partition_at_32k():
         print(f"partition {p} dropped: max shift {max_abs:.3e}, {n_bad} elements outside")
         assert n_bad > 0, f"dropping partition {p} must break the bound"
         assert max_abs < ABS_TOL["bf16"], "the absolute tolerance alone would pass it"
+
+
+def emulate_quantised_logits(q64, codes, steps, zb_keys, scale):
+    """Logits (log2 units, float32 values) the quantised-key kernels form for
+    the rows q64 [G][d] over keys code * step (+ zero points): q' = q * step in
+    float32, scaled by 2^(14 - e) so the row's largest |q'| lies in [2^13,
+    2^14), rounded to f16 (the B operand), summed against the exact codes in
+    float32, the power of two and scale * log2(e) folded back; the zero
+    points' share (2-bit keys) added in float32."""
+    qp = (q64.astype(np.float32) * steps.astype(np.float32)).astype(np.float64)
+    out = np.empty((q64.shape[0], codes.shape[0]))
+    qs = np.float32(np.float32(scale) * np.float32(LOG2E))
+    for r in range(q64.shape[0]):
+        mx = np.abs(qp[r]).max()
+        e = int(np.frexp(mx)[1]) if mx > 0 else 0
+        op = (qp[r] * 2.0 ** (14 - e)).astype(np.float16).astype(np.float64)
+        dots = (codes.astype(np.float64) @ op).astype(np.float32).astype(np.float64) * 2.0 ** (e - 14)
+        if zb_keys is not None:
+            dots = dots + float(np.float32(q64[r] @ zb_keys))
+        out[r] = (dots.astype(np.float32) * qs).astype(np.float32)
+    return out
+
+
+@pytest.mark.parametrize("kind,dtype", [("k8", "f16"), ("k2", "f16"), ("k8", "bf16")])
+def test_quantised_gates_admit_the_f16_query_rounding(kind, dtype):
+    """The widened gate (quantised_gates) admits the rounding of the f16 query
+    operand of int8 and 2-bit keys on top of the kernel's other rounding, on
+    rows with the key outlier channels of the workloads (the f16 unit alone
+    is not guaranteed to), and still rejects the output with one 16-token
+    block dropped at 4096 tokens."""
+    from oracle import quantized_kv as qk
+    from parity_bounds import quantised_gates
+    w = shaped_case(21, dtype=dtype, hq=16, hkv=4, lens=[1500, 4096])
+    G = w.group
+    got, want, mag, dropped = [], [], 0.0, []
+    if kind == "k8":
+        pool, steps = wl.k8_inputs(w, 22, outlier_columns=2)
+    else:
+        pool, steps, zeros = wl.k2_inputs(w, 23, outlier_columns=2)
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        for g in range(w.num_kv_heads):
+            if kind == "k8":
+                codes = oracle.k_rows(pool, w.block_tables[s], L, g).astype(np.float64)
+                K = codes * steps[g].astype(np.float64)
+                zk = None
+            else:
+                codes = qk.k2_rows(pool, w.block_tables[s], L, g).astype(np.float64)
+                K = zeros[g].astype(np.float64) + codes * steps[g].astype(np.float64)
+                zk = zeros[g].astype(np.float64)
+            V = oracle.widen(oracle.v_rows(w.v_pool, w.block_tables[s], L, g), dtype)
+            q64 = oracle.widen(w.q[s, g * G:(g + 1) * G], dtype)
+            x32 = emulate_quantised_logits(q64, codes, steps[g], zk, w.scale)
+            acc, lsum, _ = emulate_range(x32, V, dtype)
+            got.append(round_to((acc / lsum[:, None]).astype(np.float32), dtype))
+            x = float(np.float32(w.scale)) * (q64 @ K.T)
+            p = np.exp(x - x.max(axis=1, keepdims=True))
+            want.append((p @ V) / p.sum(axis=1, keepdims=True))
+            if L == 4096:  # the same rows with logical block 100 dropped
+                keep = np.ones(L, bool)
+                keep[1600:1616] = False
+                pd = np.exp(x[:, keep] - x[:, keep].max(axis=1, keepdims=True))
+                dropped.append((len(got) - 1, (pd @ V[keep]) / pd.sum(axis=1, keepdims=True)))
+            mag = max(mag, float(np.float32(w.scale)) *
+                      float((np.abs(q64) @ np.abs(codes * steps[g]).T).max()))
+    got_list = got
+    got, want = np.concatenate(got), np.concatenate(want)
+    vmax = float(np.abs(oracle.widen(w.v_pool, dtype)[np.isfinite(oracle.widen(w.v_pool, dtype))]).max())
+    gates = quantised_gates(dtype, mag, vmax)
+    n_bad, max_abs, ratio = violations(got, want, dtype, **gates)
+    plain = violations(got, want, dtype)[2]
+    print(f"{kind}-{dtype}: max-abs {max_abs:.3e}, err/widened bound {ratio:.3f}, "
+          f"err/plain bound {plain:.3f}, logit magnitude {mag:.1f}")
+    assert n_bad == 0
+    assert ratio < 0.8, "the emulated rounding must leave a margin under the widened bound"
+    # still discriminating: a dropped 16-token block at 4096 tokens breaks it
+    caught = sum(violations(got_rows, want_drop, dtype, **gates)[0] > 0
+                 for got_rows, want_drop in ((got_list[i], wd) for i, wd in dropped))
+    assert caught == len(dropped) > 0, "dropping a block must break the widened bound"
