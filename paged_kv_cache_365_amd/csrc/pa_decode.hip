@@ -269,7 +269,8 @@ struct MmaF32 {
 // f16 steps, the low 8 channels against q operand 0 and the high 8 against
 // operand 1.  The B operand is q' = q * scale per channel (times a power of
 // two per row, taken out again on the logits), rounded to f16; the codes
-// convert to f16 exactly, so the matrix cores see exact integers.
+// convert to f16 exactly (biased by a constant the logit removes once per row,
+// see codes()), so the matrix cores see exact values.
 template <class VM>
 struct MmaK8 {
   static constexpr int kKBytes = 1;
@@ -279,18 +280,26 @@ struct MmaK8 {
   static constexpr int kQOps = 2;
   using VLoad = typename VM::VLoad;
   using POp = typename VM::POp;
-  // 8 int8 codes (two words) -> f16x8.  code ^ 0x80 is the offset-binary byte
-  // u = code + 128; the f16 with bits 0x6400 | u is 1024 + u, so subtracting
-  // 1152 leaves the code (all integers below 2048 are exact in f16).
+  // 8 int8 codes (two words) -> f16x8, biased.  code ^ 0x80 is the
+  // offset-binary byte u = code + 128, and the f16 with bits 0x5800 | u is
+  // 128 + u / 8 = 144 + code / 8, exact (eight bits of a ten-bit mantissa).
+  // The bias is not subtracted per code: the logit products sum
+  // 144 Q + (1/8) sum_c q'_c code_c with Q = sum_c q'_c, so the kernel takes
+  // the logit as 8 qs * sum - 1152 qs Q in one fused multiply-add (kCodeMul,
+  // kCodeOffset; Q from the row's rounded operands).  The bias costs at most a
+  // few units in the f32 sums' last places of 144 Q -- far below the f16
+  // rounding of q' itself.
+  static constexpr float kCodeMul = 8.f;
+  static constexpr float kCodeOffset = 1152.f;
   static __device__ __forceinline__ f16x8 codes(uint32_t w0, uint32_t w1) {
     w0 ^= 0x80808080u;
     w1 ^= 0x80808080u;
-    constexpr uint32_t kExp = 0x64646464u;
+    constexpr uint32_t kExp = 0x58585858u;
     const u32x4 h = {__builtin_amdgcn_perm(kExp, w0, 0x04010400u),
                      __builtin_amdgcn_perm(kExp, w0, 0x04030402u),
                      __builtin_amdgcn_perm(kExp, w1, 0x04010400u),
                      __builtin_amdgcn_perm(kExp, w1, 0x04030402u)};
-    return __builtin_bit_cast(f16x8, h) - static_cast<_Float16>(1152.0f);
+    return __builtin_bit_cast(f16x8, h);
   }
   static __device__ __forceinline__ f32x4 qk(const uint4& k, const uint4* q, f32x4 c) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes(k.x, k.y), __builtin_bit_cast(f16x8, q[0]), c,
@@ -315,12 +324,11 @@ struct MmaK8 {
 // step j is word j / 2, half j % 2 (bits 8 and up of the word, shifted down
 // by 8, for half 1), and (word & (0x30003 << 2i)) keeps the codes of the pair
 // e = 2i, 2i + 1 in place, at bits 2i and 16 + 2i.  Or-ing in 0x6400 makes each
-// half the f16 1024 + code * 4^i (at most 1216: exact), and subtracting 1024
-// leaves code * 4^i exactly -- no shift per pair.  The B operand is
-// q' = q * step per channel (times a power of two per row, as for int8 keys)
-// times 4^-i for the elements of pair i, so the products are unchanged; the
-// zero points add the same scale * sum_c q_c z_c to every logit of a row
-// (kept in qb).
+// half the f16 1024 + code * 4^i (at most 1216: exact) -- no shift per pair.
+// The B operand is q' = q * step per channel (times a power of two per row, as
+// for int8 keys) times 4^-i for the elements of pair i, so the products are
+// q'_c code_c plus the bias (see codes()); the zero points add the same
+// scale * sum_c q_c z_c to every logit of a row (kept in qb).
 template <class VM, int D>
 struct MmaK2 {
   static constexpr int kKBytes = 0;  // sub-byte keys
@@ -337,12 +345,18 @@ struct MmaK2 {
       return k;
     }
   }
+  // The 1024 bias of each half stays in: the products sum
+  // 1024 Q + sum_c q'_c code_c (Q = sum_c of the rounded operands), and the
+  // kernel subtracts 1024 qs Q once per row inside the fused multiply-add of
+  // the logit (kCodeOffset).
+  static constexpr float kCodeMul = 1.f;
+  static constexpr float kCodeOffset = 1024.f;
   static __device__ __forceinline__ f16x8 codes(uint32_t w, int h) {
     const uint32_t x = h ? (w >> 8) : w;
     u32x4 v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = (x & (0x00030003u << (2 * i))) | 0x64006400u;
-    return __builtin_bit_cast(f16x8, v) - static_cast<_Float16>(1024.0f);
+    return __builtin_bit_cast(f16x8, v);
   }
   static __device__ __forceinline__ f32x4 qk(const KLoad& k, const uint4* q, f32x4 c) {
 #pragma unroll
@@ -551,6 +565,7 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
       }
       const float up = ldexpf(1.f, 14 - ex);
       qs[c] *= ldexpf(1.f, ex - 14);
+      float qsum = 0.f;
 #pragma unroll
       for (int j = 0; j < kKLoads; ++j) {
 #pragma unroll
@@ -558,10 +573,15 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
           f16x8 h;
 #pragma unroll
           for (int t = 0; t < 8; ++t) h[t] = static_cast<_Float16>(qp[j][8 * hh + t] * up);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) qsum += static_cast<float>(h[t]);
           const uint4 v = __builtin_bit_cast(uint4, h);
           qop[c][2 * j + hh] = live ? v : make_uint4(0u, 0u, 0u, 0u);
         }
       }
+      qsum = sum_over_q(live ? qsum : 0.f);
+      qb[c] = -M::kCodeOffset * qs[c] * qsum;
+      qs[c] *= M::kCodeMul;
     } else {
       // 2-bit keys: operand j holds channels 32 j + 8 qg .. + 7 of q' = q * step,
       // scaled as for int8 keys; the lane's share of sum_c q_c z_c joins the
@@ -597,14 +617,20 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
       const float up = ldexpf(1.f, 14 - ex);
       qb[c] = zb * qs[c];
       qs[c] *= ldexpf(1.f, ex - 14);
+      float qsum = 0.f;
 #pragma unroll
       for (int j = 0; j < kQOps; ++j) {
         f16x8 h;
 #pragma unroll
         for (int t = 0; t < 8; ++t) h[t] = static_cast<_Float16>(qp[j][t] * up * ldexpf(1.f, -2 * (t >> 1)));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qsum += static_cast<float>(h[t]);
         const uint4 v = __builtin_bit_cast(uint4, h);
         qop[c][j] = live ? v : make_uint4(0u, 0u, 0u, 0u);
       }
+      qsum = sum_over_q(live ? qsum : 0.f);
+      qb[c] -= M::kCodeOffset * qs[c] * qsum;
+      qs[c] *= M::kCodeMul;
     }
     row_hi[c] = live ? min(t_hi, Lc - T + 1 + i) : t_hi;
   }
@@ -693,11 +719,12 @@ __global__ __launch_bounds__(kWaves * 64, (min_waves_per_simd<M, D, kChunks, kLd
 #pragma unroll
       for (int j = 0; j < kKLoads; ++j) sc = M::qk(kr[j], &qop[c][j * M::kQOps], sc);
       float x[4];
+      if constexpr (M::kKBits < 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs[c];
-      if constexpr (M::kKBits == 2) {
+        for (int i = 0; i < 4; ++i) x[i] = fmaf(sc[i], qs[c], qb[c]);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] += qb[c];
+        for (int i = 0; i < 4; ++i) x[i] = sc[i] * qs[c];
       }
       if (masked) {
         const int n = min(max(row_hi[c] - tok0, 0), 4);
