@@ -149,6 +149,49 @@ def test_decode_k8_tiny_and_huge_scales():
         assert np.abs(widen_f32(out) - want).max() <= TOL, factor
 
 
+@pytest.mark.parametrize("dtype,sign,P", [("f16", 1.0, 0), ("f16", -1.0, 64), ("bf16", 1.0, 64)])
+def test_decode_k8_same_sign_query(dtype, sign, P):
+    """Every query element of one sign: the sum Q of a row's operands -- and
+    with it the code bias 144 Q the kernel removes once per row -- is as large
+    as it gets, so the float32 cancellation is at its worst.  Outputs within
+    the gates widened by the f16 query rounding, partial lse within its bound."""
+    from parity_bounds import quantised_gates
+    d, hq, hkv = 128, 16, 2
+    lens = [1, 17, 300, 1000]
+    w = wl.make_random_case(741, num_seqs=len(lens), num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=d, dtype=dtype, lens=lens)
+    codes, scale = wl.k8_inputs(w, 742, outlier_columns=2)
+    rng = np.random.default_rng(743)
+    q = wl.f64_to_storage(sign * (np.abs(rng.standard_normal((len(lens), 1, hq, d))) + 0.5), dtype)
+    dw = upload(w, DEV)
+    ws = None
+    if P:
+        n = pa.pa_decode_workspace_bytes(len(lens), hq, d, w.max_context_len, P)
+        ws = torch.empty(n // 4, dtype=torch.float32, device=DEV)
+    out = pa.k8_attention(to_torch(q, dtype, DEV), k8_tensor(codes), dw.v_pool, f32_tensor(scale),
+                          dw.block_tables, dw.context_lens, w.max_context_len, w.scale,
+                          partition_size=P, workspace=ws)
+    torch.cuda.synchronize()
+    want = qk.paged_decode_k8(q, codes, w.v_pool, w.block_tables, w.context_lens, w.scale, scale,
+                              dtype)
+    bound = lse_bound(q, codes, scale, w, dtype)
+    qmag = float((bound - WEIGHT_U[dtype] - 1e-4).max()) * 2.0 ** 11
+    v = oracle.widen(w.v_pool, dtype)
+    gates = quantised_gates(dtype, qmag, float(np.abs(v[np.isfinite(v)]).max()))
+    assert_parity(widen_f32(out), want, dtype, f"int8 keys, same-sign query {dtype} P{P}", **gates)
+    if P:
+        n_parts = oracle.num_partitions(w.max_context_len, P)
+        rows = len(lens) * hq
+        lse_p = ws.cpu().numpy()[rows * n_parts * d: rows * n_parts * (d + 1)].reshape(
+            len(lens), hq, n_parts)
+        _, wlse = qk.paged_decode_k8_partials(q, codes, w.v_pool, w.block_tables, w.context_lens,
+                                              w.scale, scale, dtype, P, w.max_context_len)
+        live = np.isfinite(wlse)
+        assert np.array_equal(np.isfinite(lse_p), live)
+        b = np.broadcast_to(bound[:, :, None], wlse.shape)
+        assert (np.abs(lse_p[live] - wlse[live]) <= b[live]).all()
+
+
 def test_block_moves_and_init_on_k8_pools():
     rng = np.random.default_rng(40)
     nb, hkv, d = 12, 4, 128
