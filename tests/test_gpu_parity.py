@@ -397,3 +397,38 @@ def test_split_one_wave_per_partition(dtype, hq, hkv, T, P, bs):
     assert np.abs(lse_p[live] - wlse[live]).max(initial=0) <= LSE_TOL[dtype]
     assert_close(o_p[live], wo[live], TOL[dtype], "partials")
     assert not o_p[~live].any()
+
+
+def test_split_workspace_past_2_31_elements():
+    """Index arithmetic past 32 bits: 1024 sequences x 64 query heads x 4096
+    tokens cut into 256 partitions of 16 tokens give 2.16e9 partial floats
+    (8.7 GB of workspace), so the rows of the last sequences sit past element
+    2^31 of it.  Every sequence reads the same 256 blocks (a small pool; the
+    gather still goes through each sequence's table).  All 64 heads of the
+    first, a middle and the last sequence against the oracle."""
+    B, hq, hkv, d, L, P, dtype = 1024, 64, 8, 128, 4096, 16, "bf16"
+    nb = L // 16 + 8
+    rng = np.random.default_rng(1201)
+    kshape, vshape = wl.pool_shapes(nb, hkv, d, dtype)
+    k_pool = wl.normal(rng, kshape, dtype)
+    v_pool = wl.normal(rng, vshape, dtype)
+    perm = rng.permutation(nb).astype(np.int32)[: L // 16]
+    tables = np.tile(perm, (B, 1))
+    lens = np.full(B, L, np.int32)
+    q = wl.normal(rng, (B, hq, d), dtype)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    n = pa.pa_decode_workspace_bytes(B, hq, d, L, P)
+    assert n // 4 > 2 ** 31
+    ws = torch.empty(n // 4, dtype=torch.float32, device=DEV)
+    out = pa.paged_attention(to_torch(q, dtype, DEV), to_torch(k_pool, dtype, DEV),
+                             to_torch(v_pool, dtype, DEV), torch.from_numpy(tables).to(DEV),
+                             torch.from_numpy(lens).to(DEV), L, scale, partition_size=P,
+                             workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    got = widen_f32(out)
+    seqs = [0, 511, B - 1]
+    pairs = [(s, h) for s in seqs for h in range(hq)]
+    want = oracle.paged_decode(q, k_pool, v_pool, tables, lens, scale, dtype, pairs=pairs)
+    assert_parity(got[seqs], want[seqs], dtype, "1024 x 4096 tokens in 16-token partitions "
+                  "(2.16e9 partial floats)")
