@@ -432,3 +432,41 @@ def test_split_workspace_past_2_31_elements():
     want = oracle.paged_decode(q, k_pool, v_pool, tables, lens, scale, dtype, pairs=pairs)
     assert_parity(got[seqs], want[seqs], dtype, "1024 x 4096 tokens in 16-token partitions "
                   "(2.16e9 partial floats)")
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_pool_offsets_past_2_31_elements(P):
+    """Index arithmetic past 32 bits in the pool: 140000 blocks of 8 KV heads x
+    16 tokens x 128 channels hold 2.29e9 elements per pool (4.6 GB each), and
+    the tables point at the last 300 of them, whose tiles start past element
+    2^31.  The big pools are filled on the GPU; the oracle runs on a compact
+    copy of the same 300 blocks under a relabelling (which leaves attention
+    unchanged)."""
+    hq, hkv, d, dtype = 32, 8, 128, "bf16"
+    nb, used = 140000, 300
+    assert nb * hkv * 16 * d > 2 ** 31
+    rng = np.random.default_rng(1301)
+    kshape, vshape = wl.pool_shapes(used, hkv, d, dtype)
+    kc = wl.normal(rng, kshape, dtype)
+    vc = wl.normal(rng, vshape, dtype)
+    lens = np.array([1000, 37, 999, 16], np.int32)
+    steps = [(int(L) + 15) // 16 for L in lens]
+    ids = rng.permutation(used).astype(np.int32)
+    tables_c = np.full((len(lens), max(steps)), -1, np.int32)
+    at = 0
+    for s, n in enumerate(steps):
+        tables_c[s, :n] = ids[at:at + n]
+        at += n
+    tables_big = np.where(tables_c >= 0, tables_c + (nb - used), -1).astype(np.int32)
+    big_k = torch.zeros((nb,) + kshape[1:], dtype=TORCH_DTYPE[dtype], device=DEV)
+    big_v = torch.zeros((nb,) + vshape[1:], dtype=TORCH_DTYPE[dtype], device=DEV)
+    big_k[nb - used:] = to_torch(kc, dtype, DEV)
+    big_v[nb - used:] = to_torch(vc, dtype, DEV)
+    q = wl.normal(rng, (len(lens), hq, d), dtype)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    out = pa.paged_attention(to_torch(q, dtype, DEV), big_k, big_v,
+                             torch.from_numpy(tables_big).to(DEV), torch.from_numpy(lens).to(DEV),
+                             int(lens.max()), scale, partition_size=P)
+    torch.cuda.synchronize()
+    want = oracle.paged_decode(q, kc, vc, tables_c, lens, scale, dtype)
+    assert_parity(widen_f32(out), want, dtype, f"pool of {nb} blocks, tiles past 2^31 (P{P})")
